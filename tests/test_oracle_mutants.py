@@ -1,0 +1,50 @@
+"""Planted mistakes in the oracle must be caught by its pins.
+
+Each mutant is a copy of ``oracle/attn_oracle.c`` with one plausible slip
+(a dropped term, a wrong sign, scale or index, a transposed layout, a wrong
+tie rule).  It is built into a temporary library and the oracle pin tests are
+run against it in a subprocess; every mutant has to make them fail.  The
+mistakes live only in those temporary copies, on the CPU.
+"""
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+SRC = os.path.join(ROOT, "oracle", "attn_oracle.c")
+
+MUTANTS = {
+    "scale_1_over_d": ("w[j] = acc / sqrt_d;", "w[j] = acc / 128.0;"),
+    "exp_sign": ("w[j] = exp(w[j] - m);", "w[j] = exp(m - w[j]);"),
+    "drop_first_dim": ("for (int c = 0; c < D; ++c)\n            acc += qrow[c] * kr[c];",
+                       "for (int c = 1; c < D; ++c)\n            acc += qrow[c] * kr[c];"),
+    "no_normalisation": ("o[c] = acc[c] / l;", "o[c] = acc[c];"),
+    "reversed_weights": ("acc[c] += w[j] * vr[c];", "acc[c] += w[Sk - 1 - j] * vr[c];"),
+    "bshd_as_bhsd": ("return ((b * S + s) * H + h) * D + c;", "return ((b * H + h) * S + s) * D + c;"),
+    "q_head_index_swapped": ("qrow[c] = oracle_bf16_decode(jb->q[offset_of(jb->layout, jb->H, jb->Sq, jb->b, jb->h, i, c)]);",
+                             "qrow[c] = oracle_bf16_decode(jb->q[offset_of(jb->layout, jb->H, jb->Sq, jb->b, (jb->h + 1) % jb->H, i, c)]);"),
+    "rtne_tie_to_odd": ("fmod(f, 2.0) == 1.0", "fmod(f, 2.0) == 0.0"),
+    "rtna_strict": ("if (r >= 0.5)", "if (r > 0.5)"),
+    "decode_bias": ("mag = ldexp((double)(128 + f), e - 127 - 7);", "mag = ldexp((double)(128 + f), e - 126 - 7);"),
+    "no_subnormal_clamp": ("if (e < -126)\n        e = -126;", ""),
+    "overflow_rtz_to_inf": ("return mode == OR_RTZ ? (sign | 0x7F7F) : (sign | 0x7F80);", "return sign | 0x7F80;"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mut = tmp_path / "attn_oracle_mutant.c"
+    mut.write_text(src.replace(old, new))
+    lib = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-pthread",
+                    str(mut), "-lm", "-o", str(lib)], check=True)
+    env = dict(os.environ, ORACLE_LIB=str(lib))
+    r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
+                        "tests/test_oracle_attention.py", "tests/test_oracle_rounding.py"],
+                       cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
+    assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
