@@ -1,0 +1,119 @@
+"""Fused non-causal bf16 forward attention (head_dim 128) for MI355X.
+
+Thin binding over the C ABI in ``include/attn_fwd.h``: argument marshalling
+only, every step of the computation runs in the HIP library
+``libattn_fwd.so``.  PyTorch is used for device memory and streams.
+
+    attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
+    attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne") -> torch.Tensor
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "attn_fwd_bf16", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
+    "AttnError", "LAYOUTS", "ROUND_MODES", "library_path", "load_library",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libattn_fwd.so")
+
+# values of attn_layout_t / attn_round_t in include/attn_fwd.h
+LAYOUTS = {"bshd": 0, "bhsd": 1}
+ROUND_MODES = {"rtne": 0, "rtna": 1, "rtz": 2}
+HEAD_DIM = 128
+
+_lib = None
+
+
+class AttnError(RuntimeError):
+    def __init__(self, status: int):
+        self.status = status
+        super().__init__(f"attn_fwd_bf16 failed ({status}): {attn_fwd_bf16_strerror(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load the built HIP library; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                f"{_LIB_PATH} is missing: build it with `python -m bf16_forward_attention_amd.build` "
+                "(there is no fallback implementation)")
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64 = ctypes.c_void_p, ctypes.c_int64
+        lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+        lib.attn_fwd_bf16.restype = ctypes.c_int
+        lib.attn_fwd_bf16_strerror.argtypes = [ctypes.c_int]
+        lib.attn_fwd_bf16_strerror.restype = ctypes.c_char_p
+        lib.attn_fwd_bf16_abi_version.argtypes = []
+        lib.attn_fwd_bf16_abi_version.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def attn_fwd_bf16(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int,
+                  layout: int, round_mode: int, stream: int) -> int:
+    """The C entry point with raw device addresses; returns the status code."""
+    return load_library().attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream)
+
+
+def attn_fwd_bf16_strerror(status: int) -> str:
+    return load_library().attn_fwd_bf16_strerror(status).decode()
+
+
+def attn_fwd_bf16_abi_version() -> int:
+    return load_library().attn_fwd_bf16_abi_version()
+
+
+def _dims(q, k, layout: str):
+    if layout == "bshd":
+        B, Sq, H, d = q.shape
+        Bk, Sk, Hk, dk = k.shape
+    elif layout == "bhsd":
+        B, H, Sq, d = q.shape
+        Bk, Hk, Sk, dk = k.shape
+    else:
+        raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {layout!r}")
+    if d != HEAD_DIM or dk != HEAD_DIM or Bk != B or Hk != H:
+        raise ValueError(f"incompatible shapes q{tuple(q.shape)} k{tuple(k.shape)} for layout {layout}")
+    return B, H, Sq, Sk
+
+
+def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None):
+    """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
+
+    ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H,128] for "bshd", or
+    [B,H,S,128] for "bhsd"; all contiguous bf16 on one device.  Enqueued on
+    ``stream`` (default: torch's current stream on that device).
+    """
+    import torch
+
+    if round_mode not in ROUND_MODES:
+        raise ValueError(f"round_mode must be one of {sorted(ROUND_MODES)}, got {round_mode!r}")
+    B, H, Sq, Sk = _dims(q, k, layout)
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("v must have the shape of k")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
+        if t.device != q.device:
+            raise ValueError("q, k and v must be on one device")
+    if out is None:
+        out = torch.empty_like(q)
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
+                               LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
+    if status != 0:
+        raise AttnError(status)
+    return out

@@ -1,0 +1,103 @@
+/*
+ * attn_fwd.h -- C ABI of the MI355X (gfx950) fused bf16 forward attention.
+ *
+ * Operation (snilld.dk page "Open source attention kernel in HIP beats AITER
+ * v3 on MI300X", section "Hvordan kernen arbejder" / How the kernel works):
+ * for every batch b, head h and query row i,
+ *
+ *     O[b,h,i,:] = softmax_j( Q[b,h,i,:] . K[b,h,j,:] / sqrt(128) ) V[b,h,j,:]
+ *
+ * non-causal, head_dim fixed at 128, one head count shared by Q, K and V, any
+ * query length Sq and key length Sk (cross-attention allowed), inputs read in
+ * the BSHD or BHSD layout without a transpose (same page, section "Hvad er
+ * udgivet" / What was released).  Output is bf16, rounded per call in one of
+ * three modes (tilnote.io page on the MoonMath HIP attention kernel, section
+ * on its performance figures; snilld.dk page, section "Numerik samlet et
+ * sted" / Numerics in one place).
+ *
+ * Numerics: logits and softmax in fp32, both products on bf16 matrix cores
+ * with fp32 accumulation, the softmax weights rounded to bf16 (nearest-even)
+ * for the second product, and one final rounding of each fp32 output to bf16
+ * in the requested mode.  Results are deterministic: repeated calls on the
+ * same inputs give identical bits.  A NaN logit makes its query row NaN; a
+ * +Inf logit makes its row NaN; a -Inf logit removes that key from the row.
+ *
+ * Layout (element offsets, d = 128, all four tensors contiguous, O shaped
+ * like Q):
+ *     BSHD: Q/O [B, Sq, H, 128], K/V [B, Sk, H, 128];
+ *           (b, s, h, c) at ((b*S + s)*H + h)*128 + c
+ *     BHSD: Q/O [B, H, Sq, 128], K/V [B, H, Sk, 128];
+ *           (b, h, s, c) at ((b*H + h)*S + s)*128 + c
+ *
+ * Ownership: the caller owns every buffer.  The library allocates nothing on
+ * the device, never synchronises, and keeps no state beyond a once-filled
+ * per-device architecture cache; calls are thread-safe.
+ */
+#ifndef ATTN_FWD_H
+#define ATTN_FWD_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ATTN_FWD_ABI_VERSION 1
+
+typedef enum {
+    ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
+    ATTN_LAYOUT_BHSD = 1  /* [B, H, S, 128] */
+} attn_layout_t;
+
+/* Output rounding, fp32 -> bf16, applied once per output element. */
+typedef enum {
+    ATTN_ROUND_RTNE = 0, /* to nearest, ties to even */
+    ATTN_ROUND_RTNA = 1, /* to nearest, ties away from zero */
+    ATTN_ROUND_RTZ = 2   /* toward zero */
+} attn_round_t;
+
+typedef enum {
+    ATTN_OK = 0,
+    ATTN_ERR_NULL = 1,   /* a tensor pointer is NULL */
+    ATTN_ERR_SIZE = 2,   /* B, H, Sq or Sk < 1, or a byte size overflows int64 */
+    ATTN_ERR_LAYOUT = 3, /* layout is not an attn_layout_t value */
+    ATTN_ERR_ROUND = 4,  /* round_mode is not an attn_round_t value */
+    ATTN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned */
+    ATTN_ERR_ALIAS = 6,  /* o overlaps q, k or v */
+    ATTN_ERR_DEVICE = 7, /* the current device is not gfx950, or cannot be queried */
+    ATTN_ERR_HIP = 8     /* the kernel launch failed */
+} attn_status_t;
+
+/*
+ * attn_fwd_bf16 -- enqueue O = softmax(Q K^T / sqrt(128)) V on `stream`.
+ *
+ *   q, k, v : device pointers to bf16 bit patterns (uint16), layout above.
+ *   o       : device pointer receiving the bf16 output, shaped like q.
+ *   B, H    : batch size and head count (>= 1).
+ *   Sq, Sk  : query and key lengths (>= 1), independent of each other.
+ *   layout  : attn_layout_t, shared by all four tensors.
+ *   round_mode : attn_round_t, the output rounding.
+ *   stream  : hipStream_t to enqueue on (NULL = the null stream).
+ *
+ * Returns ATTN_OK once the kernel is enqueued; the call is asynchronous and
+ * O is valid after the stream reaches that point.  Argument errors
+ * (ATTN_ERR_NULL .. ATTN_ERR_ALIAS) are detected before any HIP call and
+ * nothing is launched.  ATTN_ERR_DEVICE: the current device is not gfx950.
+ * ATTN_ERR_HIP: the launch was rejected.  Faults inside the kernel surface at
+ * the caller's next synchronisation, as for any HIP kernel.
+ */
+int attn_fwd_bf16(const void *q, const void *k, const void *v, void *o,
+                  int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                  int layout, int round_mode, void *stream);
+
+/* Static description of a status code (never NULL). */
+const char *attn_fwd_bf16_strerror(int status);
+
+/* ATTN_FWD_ABI_VERSION of the built library. */
+int attn_fwd_bf16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ATTN_FWD_H */

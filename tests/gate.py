@@ -1,0 +1,80 @@
+"""The parity gate between the GPU's bf16 output and the oracle.
+
+Reading of "within 2 bf16 ULP per element": the snilld.dk page asks for a
+ULP check per tensor block (section "Hvad det betyder i praksis" / What it
+means in practice); a block here is one query's 128-wide output row.  Every
+element g of a row must satisfy
+
+    |g - r| <= 2 * ulp(M),   M = max_c |o*_c|  (the row's largest exact output)
+
+where r is the oracle's bf16 in the same mode and ulp(x) = 2^(max(floor(log2 x),
+-126) - 7).  NaN positions must be identical, +Inf and -Inf positions identical
+with their signs (same page, section "Numerik samlet et sted": NaN/Inf handled
+bit-identically); those positions are excluded from the distance test.
+The per-element strict ULP distance is reported as a diagnostic.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+
+ULP_TOL = 2.0
+
+
+def decode(bits: np.ndarray) -> np.ndarray:
+    with np.errstate(invalid="ignore"):
+        return (np.asarray(bits, np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
+def row_ulp(exact: np.ndarray) -> np.ndarray:
+    """ulp of bf16 at each row's largest finite |o*| (shape [..., 1])."""
+    a = np.where(np.isfinite(exact), np.abs(exact), 0.0)
+    m = a.max(axis=-1, keepdims=True)
+    with np.errstate(divide="ignore"):
+        e = np.where(m > 0, np.floor(np.log2(np.where(m > 0, m, 1.0))), -126.0)
+    e = np.maximum(e, -126.0)
+    return np.exp2(e - 7.0)
+
+
+def ord_bf16(bits: np.ndarray) -> np.ndarray:
+    b = np.asarray(bits).astype(np.int64)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+@dataclass
+class GateResult:
+    ok: bool
+    n: int
+    violations: int
+    nan_mismatch: int
+    inf_mismatch: int
+    max_row_ulps: float
+    strict_hist: dict
+    rms_rel: float
+
+    def summary(self) -> str:
+        return (f"n={self.n} viol={self.violations} nan_mis={self.nan_mismatch} inf_mis={self.inf_mismatch} "
+                f"max_row_ulps={self.max_row_ulps:.3f} strict={self.strict_hist} rms_rel={self.rms_rel:.3e}")
+
+
+def gate(gpu_bits: np.ndarray, oracle_bits: np.ndarray, oracle_exact: np.ndarray) -> GateResult:
+    """Rows are the last axis' leading dims; all arrays shaped [..., 128]."""
+    g = decode(gpu_bits)
+    r = decode(oracle_bits)
+    nan_g, nan_r = np.isnan(g), np.isnan(r)
+    inf_g, inf_r = np.isinf(g), np.isinf(r)
+    nan_mis = int(np.sum(nan_g != nan_r))
+    inf_mis = int(np.sum((inf_g != inf_r) | (inf_g & inf_r & (np.sign(g) != np.sign(r)))))
+    fin = ~(nan_g | nan_r | inf_g | inf_r)
+    ulp = np.broadcast_to(row_ulp(oracle_exact), g.shape)
+    dist = np.where(fin, np.abs(g - r) / ulp, 0.0)
+    viol = int(np.sum(dist > ULP_TOL))
+    strict = np.where(fin, np.abs(ord_bf16(gpu_bits) - ord_bf16(oracle_bits)), 0)
+    hist = {"0": int(np.sum(fin & (strict == 0))), "1": int(np.sum(strict == 1)),
+            "2": int(np.sum(strict == 2)), ">2": int(np.sum(strict > 2))}
+    ex = np.where(fin & np.isfinite(oracle_exact), oracle_exact, 0.0)
+    scale = np.sqrt(np.mean(ex**2)) if ex.size else 0.0
+    rms = float(np.sqrt(np.mean(np.where(fin, (g - ex) ** 2, 0.0))) / scale) if scale > 0 else 0.0
+    return GateResult(viol == 0 and nan_mis == 0 and inf_mis == 0, int(fin.sum()), viol, nan_mis, inf_mis,
+                      float(dist.max()) if dist.size else 0.0, hist, rms)

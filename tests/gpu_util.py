@@ -1,0 +1,76 @@
+"""Helpers for the GPU tests: move bf16 bit arrays to the device, call the
+library through its C ABI, bring the output back as bits."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+import bf16_forward_attention_amd as attn
+from bf16_forward_attention_amd import synth
+
+MODES = ("rtne", "rtna", "rtz")
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_device(bits: np.ndarray) -> torch.Tensor:
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16)
+    return t.to("cuda:0")
+
+
+def to_bits(t: torch.Tensor) -> np.ndarray:
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def launch(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
+           stream: torch.cuda.Stream | None = None) -> None:
+    """Call attn_fwd_bf16 through the C ABI with raw device pointers."""
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Sk = k.shape[1]
+    else:
+        B, H, Sq, _ = q.shape
+        Sk = k.shape[2]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = attn.attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Sq, Sk,
+                            attn.LAYOUTS[layout], attn.ROUND_MODES[mode], s.cuda_stream)
+    if st != 0:
+        raise attn.AttnError(st)
+
+
+class Dev:
+    """Device copies of one Inputs bundle."""
+
+    def __init__(self, inp: synth.Inputs):
+        self.inp = inp
+        self.layout = inp.wl.layout
+        self.q, self.k, self.v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+        self.o = torch.empty_like(self.q)
+
+    def run(self, mode: str) -> np.ndarray:
+        """Output bits in the stored layout."""
+        launch(self.q, self.k, self.v, self.o, self.layout, mode)
+        torch.cuda.synchronize()
+        return to_bits(self.o)
+
+    def run_logical(self, mode: str) -> np.ndarray:
+        return np.ascontiguousarray(synth.to_logical(self.run(mode), self.layout))
+
+
+def run_raw(q, k, v, layout: str, mode: str) -> np.ndarray:
+    """Stored-layout bits in, stored-layout bits out."""
+    dq, dk, dv = to_device(q), to_device(k), to_device(v)
+    o = torch.empty_like(dq)
+    launch(dq, dk, dv, o, layout, mode)
+    torch.cuda.synchronize()
+    return to_bits(o)
+
+
+def run_logical(q, k, v, layout: str, mode: str) -> np.ndarray:
+    """Logical [B,H,S,128] bits in and out, stored in ``layout`` on the way."""
+    out = run_raw(synth.to_layout(q, layout), synth.to_layout(k, layout), synth.to_layout(v, layout), layout, mode)
+    return np.ascontiguousarray(synth.to_logical(out, layout))

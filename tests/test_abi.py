@@ -1,0 +1,83 @@
+"""The C ABI: the built library exports what include/attn_fwd.h declares, the
+enum values agree with the Python binding, and argument errors come back
+before any HIP call (so these run without a GPU)."""
+import os
+import re
+import subprocess
+
+import pytest
+
+import bf16_forward_attention_amd as attn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "attn_fwd.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(attn_fwd_\w+)\s*\(", text, re.M)))
+
+
+def _enum_values():
+    text = open(HEADER).read()
+    return {name: int(val) for name, val in re.findall(r"\b(ATTN_\w+)\s*=\s*(\d+)", text)}
+
+
+def test_library_exports_every_declared_symbol():
+    funcs = _declared_functions()
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_strerror"]
+    out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
+                         check=True).stdout
+    exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
+    for f in funcs:
+        assert f in exported, f
+    lib = attn.load_library()
+    for f in funcs:
+        assert hasattr(lib, f)
+
+
+def test_enum_values_match_binding():
+    ev = _enum_values()
+    assert ev["ATTN_LAYOUT_BSHD"] == attn.LAYOUTS["bshd"] and ev["ATTN_LAYOUT_BHSD"] == attn.LAYOUTS["bhsd"]
+    assert ev["ATTN_ROUND_RTNE"] == attn.ROUND_MODES["rtne"]
+    assert ev["ATTN_ROUND_RTNA"] == attn.ROUND_MODES["rtna"]
+    assert ev["ATTN_ROUND_RTZ"] == attn.ROUND_MODES["rtz"]
+
+
+def test_abi_version_and_strerror():
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_abi_version() == int(re.search(r"ATTN_FWD_ABI_VERSION\s+(\d+)", open(HEADER).read()).group(1))
+    for name, code in ev.items():
+        if name.startswith("ATTN_ERR") or name == "ATTN_OK":
+            assert attn.attn_fwd_bf16_strerror(code) and attn.attn_fwd_bf16_strerror(code) != "unknown status"
+    assert attn.attn_fwd_bf16_strerror(12345) == "unknown status"
+
+
+A, B_, C, O_ = 0x10000, 0x20000, 0x30000, 0x40000  # distinct aligned fake addresses (never dereferenced)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 1, 1, 1, 1, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, 0, 1, 1, 1, 1, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 0, 1, 1, 1, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 1, 1, 0, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, -3, 1, 1, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1 << 40, 1 << 20, 1, 1, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 2, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 1, 1, 1, 1, -1, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, 3), "ATTN_ERR_ROUND"),
+    ((A + 2, B_, C, O_, 1, 1, 1, 1, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, O_ + 8, 1, 1, 1, 1, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, A + 128, 1, 1, 1, 1, 0, 0), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, B_ - 128, 1, 1, 1, 4, 0, 0), "ATTN_ERR_ALIAS"),
+])
+def test_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16(*args, 0) == ev[code]
+
+
+def test_binding_rejects_missing_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(attn, "_lib", None)
+    monkeypatch.setattr(attn, "_LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(ImportError):
+        attn.load_library()
