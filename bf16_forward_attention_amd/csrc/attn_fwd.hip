@@ -32,7 +32,8 @@
 // Numerics.  Logits accumulate in fp32 on the matrix cores.  The softmax runs
 // in the base-2 domain: t = s * log2(e)/sqrt(128) (one fp32 constant), the
 // running maximum m starts at -FLT_MAX (finite, so an all -Inf prefix never
-// forms -Inf - -Inf), p = exp2(t - m) on the hardware exp, the row sum l in
+// forms -Inf - -Inf) and is kept rounded up so the maximal key's weight is
+// never above 1, p = exp2(t - m) on the hardware exp, the row sum l in
 // fp32 from the unrounded p.  P is rounded to bf16 (nearest-even) for the
 // second product.  The epilogue multiplies by 1/l and rounds once to bf16 in
 // the requested mode.
@@ -74,16 +75,13 @@ struct Geometry {
 };
 
 // Combine a per-lane value with the one held 32 lanes away (the other half of
-// the wave) using v_permlane32_swap: with both operands = x the two results
-// hold the low half's and the high half's values in every lane.
-__device__ __forceinline__ float wave_half_max(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
-  return fmaxf(__builtin_bit_cast(float, r[0]), __builtin_bit_cast(float, r[1]));
-}
-__device__ __forceinline__ float wave_half_sum(float x) {
-  auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(int, x), __builtin_bit_cast(int, x), false, false);
-  return __builtin_bit_cast(float, r[0]) + __builtin_bit_cast(float, r[1]);
-}
+// the wave).  This goes through ds_bpermute: AMD clang 22 folds
+// fmaxf(r[0], r[1]) of __builtin_amdgcn_permlane32_swap(x, x) into r[0], as
+// if the swap of a register with itself were the identity, which leaves the
+// two halves with different values.
+__device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
+// fp32 addition is commutative, so both halves get identical bits
+__device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
 
 template <int MODE>
 __device__ __forceinline__ uint16_t round_to_bf16(float x) {
@@ -228,7 +226,13 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int n = 0; n < 16; ++n) mx = fmaxf(mx, s[kb][n]);
     mx = wave_half_max(mx);
-    const float m_new = fmaxf(m_run, mx * kScaleLog2);
+    // The new maximum is the scaled row maximum rounded up by at least half
+    // an ulp: then fma(s, c, -m) <= 0 for the maximal logit, its weight is
+    // exp2(<= 0) <= 1 and rounds to exactly 1 in bf16, so a row dominated by
+    // one key (or with a single key) returns that V row exactly in every mode.
+    // (-Inf / NaN maxima give NaN here, which fmaxf ignores.)
+    const float mx_scaled = mx * kScaleLog2;
+    const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(mx_scaled), 0x1p-23f, mx_scaled));
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     m_run = m_new;
 
