@@ -49,6 +49,9 @@ def parse():
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for the sample")
     p.add_argument("--parity-rows", type=int, default=256)
+    p.add_argument("--calibrate-copy-mib", type=int, default=0,
+                   help="also run one device-to-device copy of this many MiB (a reference kernel of known "
+                        "traffic for the FETCH_SIZE/WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -162,6 +165,16 @@ def main():
     achieved = flops / (per.mean() * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall_ms / args.steps:.3f}), per-launch mean {per.mean():.3f} "
         f"median {np.median(per):.3f} min {per.min():.3f} ms -> {value:.1f} TFLOP/s")
+
+    if args.calibrate_copy_mib:
+        n = args.calibrate_copy_mib << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
+        del src, dst
 
     out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     result = {

@@ -9,10 +9,10 @@
 //
 // Work decomposition.  One workgroup of 4 wave64s owns BM = 128 query rows of
 // one (batch, head); each wave owns 32 of them.  Keys stream in tiles of
-// BN = 64 through LDS.  Both products run on v_mfma_f32_32x32x16_bf16 in the
-// transposed orientation
+// BN = 64.  Both products run on v_mfma_f32_32x32x16_bf16 in the transposed
+// orientation
 //     S^T (keys x queries)  = K   . Q^T      A = K tile (LDS), B = Q (VGPRs)
-//     O^T (dims x queries) += V^T . P^T      A = V^T tile (LDS), B = P (VGPRs)
+//     O^T (dims x queries) += V^T . P^T      A = V tile read transposed (LDS), B = P (VGPRs)
 // so that every lane owns exactly one query row: the softmax row statistics
 // are per-lane scalars plus one exchange between the two 32-lane halves, and
 // the rescale of the output accumulator is a per-lane multiply.
@@ -22,21 +22,36 @@
 //     B[k][j]: lane supplies column j = l % 32, k = 8g .. 8g+7
 //     C[i][j]: lane holds column j = l % 32, rows 8r + 4g + t in element 4r + t
 //
-// Key order inside a 32-key block.  The LDS K tile stores key
-// pi(i) = 16*(i/4 % 2) + 4*(i/8) + i%4 in row i, so that after the first
-// product lane group g holds the 16 consecutive keys 16g .. 16g+15 of the
-// block in elements 0..15.  Eight of those consecutive keys are exactly a
-// B operand for the second product, and the matching A operand is 8
-// consecutive keys of one V^T row: one 16-byte LDS read.
+// Data movement.  K and V tiles go from HBM straight into LDS with
+// buffer_load_dwordx4 ... lds (lane l of a load lands at 16*l past the
+// wave's LDS base), two stages deep, one workgroup barrier per tile.  The
+// buffer descriptor of each tile ends at the last valid key, so keys past Sk
+// read as zeros without any per-lane test.  LDS rows are 256 bytes, with the
+// 16-byte chunks XOR-swizzled by row so the MFMA operand reads are free of
+// bank conflicts.
+//
+// Key order inside a 32-key block.  LDS K row i holds key
+// pi(i) = 16*(i/4 % 2) + 4*(i/8) + i%4, so that after the first product lane
+// group g holds the 16 consecutive keys 16g .. 16g+15 of the block in
+// elements 0..15.  Eight of those are exactly a B operand of the second
+// product; the matching A operand (8 consecutive keys of one V column) comes
+// from two ds_read_b64_tr_b16 reads of the row-major V tile.  Within each
+// 16-lane group that instruction hands lane i element i%4 of the 8-byte
+// chunks addressed by lanes 4s + i/4 (s = 0..3); pointing lane 4s + u at keys
+// key0 + s, dims dim0 + 4u .. 4u+3 gives lane i the four keys key0 .. key0+3
+// at dim dim0 + i.
 //
 // Numerics.  Logits accumulate in fp32 on the matrix cores.  The softmax runs
 // in the base-2 domain: t = s * log2(e)/sqrt(128) (one fp32 constant), the
 // running maximum m starts at -FLT_MAX (finite, so an all -Inf prefix never
 // forms -Inf - -Inf) and is kept rounded up so the maximal key's weight is
-// never above 1, p = exp2(t - m) on the hardware exp, the row sum l in
-// fp32 from the unrounded p.  P is rounded to bf16 (nearest-even) for the
-// second product.  The epilogue multiplies by 1/l and rounds once to bf16 in
-// the requested mode.
+// never above 1, p = exp2(t - m) on the hardware exp, the row sum l in fp32
+// from the unrounded p.  The maximum (and with it the accumulator) is only
+// moved when some row's maximum grew by more than 2^8: between moves the
+// weights stay below 256, which fp32 and bf16 carry without loss of relative
+// precision.  P is rounded to bf16 (nearest-even) for the second product.
+// The epilogue multiplies by 1/l and rounds once to bf16 in the requested
+// mode.
 #include <hip/hip_runtime.h>
 
 #include <atomic>
@@ -52,18 +67,24 @@ constexpr int BM = 128;                // query rows per workgroup
 constexpr int BN = 64;                 // keys per tile
 constexpr int NWAVES = BM / 32;        // 32 query rows per wave
 constexpr int NTHREADS = NWAVES * 64;
-constexpr int K_STRIDE = D + 8;        // bf16 per K row in LDS: 272 B, 4-bank skew per row
-constexpr int VT_STRIDE = BN + 8;      // bf16 per V^T row in LDS: 144 B, 4-bank skew per row
+constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS (16 KiB)
+constexpr float kRescaleLog2 = 8.0f;   // move the running maximum only past 2^8
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
 // log2(e) / sqrt(128), rounded to fp32
 constexpr float kScaleLog2 = 0.12751743082459868f;
+// gfx9 buffer descriptor word 3: 32-bit data format, no swizzle, raw addressing
+constexpr int kBufferWord3 = 0x00020000;
 
 struct Geometry {
   int64_t q_row;   // element stride between consecutive query rows
@@ -95,17 +116,21 @@ __device__ __forceinline__ uint16_t round_to_bf16(float x) {
   return (uint16_t)(u >> 16);  // RTZ
 }
 
-// inverse of pi within a 32-key block: key a -> LDS row
-__device__ __forceinline__ int k_row_of_key(int a) {
-  return 8 * ((a & 15) >> 2) + 4 * (a >> 4) + (a & 3);
+// pi within a 32-key block: LDS row -> key
+__device__ __forceinline__ int key_of_k_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_records, kBufferWord3);
 }
 
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g) {
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * K_STRIDE];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VT_STRIDE];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE_BYTES];
 
   // ---- workgroup -> (b, h, q-tile), keeping a head's q-tiles on one XCD ----
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that
@@ -120,7 +145,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
   const int h = bh % H, b = bh / H;
 
   const int tid = threadIdx.x;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int l32 = lane & 31;
   const int grp = lane >> 5;
@@ -129,6 +154,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
   const uint16_t* Kh = K + b * g.k_batch + h * g.k_head;
   const uint16_t* Vh = V + b * g.k_batch + h * g.k_head;
   uint16_t* Oh = O + b * g.q_batch + h * g.q_head;
+  const uint32_t row_bytes = (uint32_t)(g.k_row * 2);
 
   // ---- Q fragments: this lane's query row, dims 16ks + 8grp .. +7 ----
   const int qrow = qt * BM + wave * 32 + l32;
@@ -143,42 +169,53 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
     }
   }
 
-  // ---- tile staging assignment ----
-  // K: thread covers 16-byte column chunk kc of keys kr0 + 16u (u = 0..3);
-  //    16 consecutive threads read one 256-byte key row.
-  const int kc = tid & 15, kr0 = tid >> 4;
-  // V: thread covers column chunk vc (dims 8vc .. 8vc+7) of keys 4vg .. 4vg+3,
-  //    transposed into V^T rows on the way into LDS.
-  const int vg = tid & 15, vc = tid >> 4;
+  // ---- direct-to-LDS load assignment: wave w issues loads j = 4w + u ----
+  // Load j fills LDS rows 4j .. 4j+3 (1 KiB); lane l writes row 4j + l/16 at
+  // 16-byte position l%16, which holds logical chunk (l%16) ^ swizzle(row).
+  uint32_t k_src[4], v_src[4];
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const int r = 4 * (4 * wave + u) + (lane >> 4);
+    const int p = lane & 15;
+    const int kc = p ^ (r & 15);
+    const int key = (r & 32) + key_of_k_row(r & 31);
+    k_src[u] = (uint32_t)key * row_bytes + 16u * kc;
+    const int vc = p ^ (2 * (r & 7));
+    v_src[u] = (uint32_t)r * row_bytes + 16u * vc;
+  }
 
-  u32x4 kbuf[4], vbuf[4];
-  auto load_tile = [&](int base) {
+  // ---- MFMA operand read offsets (bytes within a tile) ----
+  // K: row l32 (+32 kb), logical chunk 2ks + grp at position chunk ^ (row % 16)
+  uint32_t k_rd[8];
+#pragma unroll
+  for (int ks = 0; ks < 8; ++ks) k_rd[ks] = 256u * l32 + 16u * ((2 * ks + grp) ^ (l32 & 15));
+  // V (transposed reads): lane 16G + 4s + u reads keys 16(G/2) + 4half + s
+  // (+32kb + 8hh), dims 32db + 16(G%2) + 4u .. +3, logical chunk
+  // 4db + 2(G%2) + u/2 at position chunk ^ (2 * (row % 8))
+  uint32_t v_rd[4][2];
+  {
+    const int G = lane >> 4, sidx = (lane >> 2) & 3, u4 = lane & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int half = 0; half < 2; ++half) {
+        const int row = 16 * (G >> 1) + 4 * half + sidx;
+        const int chunk = 4 * db + 2 * (G & 1) + (u4 >> 1);
+        v_rd[db][half] = 256u * row + 16u * (chunk ^ (2 * (row & 7))) + 8u * (u4 & 1);
+      }
+  }
+
+  auto issue_loads = [&](int tile, uint8_t* kdst, uint8_t* vdst) {
+    const int base = tile * BN;
+    const int valid = Sk - base < BN ? Sk - base : BN;
+    const uint32_t nrec = (uint32_t)(valid - 1) * row_bytes + 256u;
+    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
+    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int key = base + kr0 + 16 * u;
-      kbuf[u] = key < Sk ? *(const u32x4*)(Kh + (int64_t)key * g.k_row + 8 * kc) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int key = base + 4 * vg + u;
-      vbuf[u] = key < Sk ? *(const u32x4*)(Vh + (int64_t)key * g.k_row + 8 * vc) : u32x4{0, 0, 0, 0};
-    }
-  };
-  auto store_tile = [&]() {
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int a = kr0 + 16 * u;
-      const int row = (a & 32) + k_row_of_key(a & 31);
-      *(u32x4*)(k_lds + row * K_STRIDE + 8 * kc) = kbuf[u];
-    }
-    // vbuf[u][p] holds dims (8vc + 2p, 8vc + 2p + 1) of key 4vg + u
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const uint32_t w0 = vbuf[0][p], w1 = vbuf[1][p], w2 = vbuf[2][p], w3 = vbuf[3][p];
-      u32x2 even = {(w0 & 0xFFFFu) | (w1 << 16), (w2 & 0xFFFFu) | (w3 << 16)};
-      u32x2 odd = {(w0 >> 16) | (w1 & 0xFFFF0000u), (w2 >> 16) | (w3 & 0xFFFF0000u)};
-      *(u32x2*)(vt_lds + (8 * vc + 2 * p) * VT_STRIDE + 4 * vg) = even;
-      *(u32x2*)(vt_lds + (8 * vc + 2 * p + 1) * VT_STRIDE + 4 * vg) = odd;
+      const int j = 4 * wave + u;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + 1024 * j), 16, k_src[u], 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + 1024 * j), 16, v_src[u], 0, 0, 0);
     }
   };
 
@@ -189,26 +226,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
   float l_run = 0.0f;
 
   const int n_tiles = (Sk + BN - 1) / BN;
-  load_tile(0);
-  for (int t = 0; t < n_tiles; ++t) {
-    const int base = t * BN;
-    __syncthreads();  // every wave is done reading the previous tile
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) load_tile(base + BN);  // in flight while this tile computes
 
+  auto compute_tile = [&](int t, const uint8_t* kt, const uint8_t* vt) {
+    const int base = t * BN;
     // ---- S^T = K . Q^T for the two 32-key blocks ----
-    f32x16 s[2];
+    f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
-      const uint16_t* krow = k_lds + (32 * kb + l32) * K_STRIDE + 8 * grp;
+    for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        bf16x8 a = *(const bf16x8*)(krow + 16 * ks);
+      for (int kb = 0; kb < 2; ++kb) {
+        bf16x8 a = *(const bf16x8*)(kt + k_rd[ks] + 8192 * kb);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
-    }
 
     // keys past Sk (only in the last tile) get a -Inf logit
     if (base + BN > Sk) {
@@ -226,15 +255,20 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
 #pragma unroll
       for (int n = 0; n < 16; ++n) mx = fmaxf(mx, s[kb][n]);
     mx = wave_half_max(mx);
-    // The new maximum is the scaled row maximum rounded up by at least half
-    // an ulp: then fma(s, c, -m) <= 0 for the maximal logit, its weight is
-    // exp2(<= 0) <= 1 and rounds to exactly 1 in bf16, so a row dominated by
-    // one key (or with a single key) returns that V row exactly in every mode.
-    // (-Inf / NaN maxima give NaN here, which fmaxf ignores.)
+    // The candidate maximum is the scaled row maximum rounded up by at least
+    // half an ulp: then fma(s, c, -m) <= 0 for the maximal logit, its weight
+    // is exp2(<= 0) <= 1 and rounds to exactly 1 in bf16, so a row dominated
+    // by one key (or with a single key) returns that V row exactly in every
+    // mode.  (-Inf / NaN maxima give NaN here, which fmaxf ignores.)
     const float mx_scaled = mx * kScaleLog2;
     const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(mx_scaled), 0x1p-23f, mx_scaled));
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-    m_run = m_new;
+    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleLog2) != 0) {
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      m_run = m_new;
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    }
 
     float psum = 0.0f;
     bf16x8 pf[2][2];
@@ -246,8 +280,8 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
         for (int q2 = 0; q2 < 4; ++q2) {
           const int n = 8 * hh + 2 * q2;
           f32x2 p;
-          p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n], kScaleLog2, -m_new));
-          p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n + 1], kScaleLog2, -m_new));
+          p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n], kScaleLog2, -m_run));
+          p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n + 1], kScaleLog2, -m_run));
           psum += p[0];
           psum += p[1];
           bf16x2 pb = __builtin_convertvector(p, bf16x2);
@@ -256,21 +290,35 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
         }
       }
     }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int db = 0; db < 4; ++db) acc[db] *= alpha;
+    l_run += psum;
 
     // ---- O^T += V^T . P^T ----
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const uint16_t* vrow = vt_lds + (32 * db + l32) * VT_STRIDE + 16 * grp;
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          bf16x8 a = *(const bf16x8*)(vrow + 32 * kb + 8 * hh);
+        for (int db = 0; db < 4; ++db) {
+          const uint8_t* vb = vt + 256 * (32 * kb + 8 * hh);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][0]));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][1]));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hh], acc[db], 0, 0, 0);
         }
+  };
+
+  // ---- main loop: two LDS stages, one barrier per tile ----
+  issue_loads(0, k_lds0, v_lds0);
+  for (int t = 0; t < n_tiles; t += 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t are in LDS
+    __syncthreads();                     // ... and every wave's; stage 1 is free again
+    if (t + 1 < n_tiles) issue_loads(t + 1, k_lds1, v_lds1);
+    compute_tile(t, k_lds0, v_lds0);
+    if (t + 1 < n_tiles) {
+      __builtin_amdgcn_s_waitcnt(0x0F70);
+      __syncthreads();                   // stage 0 is free again
+      if (t + 2 < n_tiles) issue_loads(t + 2, k_lds0, v_lds0);
+      compute_tile(t + 1, k_lds1, v_lds1);
     }
   }
 
@@ -332,7 +380,8 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
     return ATTN_ERR_SIZE;
   const int64_t n_qtiles = (Sq + BM - 1) / BM;
   int64_t n_wg;
-  if (!mul_ok(bh, n_qtiles, &n_wg) || n_wg > INT32_MAX || Sq > INT32_MAX || Sk > INT32_MAX || H > INT32_MAX)
+  // one 64-key tile of rows must be addressable by 32-bit buffer offsets
+  if (!mul_ok(bh, n_qtiles, &n_wg) || n_wg > INT32_MAX || Sq > INT32_MAX || Sk > INT32_MAX || H > (1 << 20))
     return ATTN_ERR_SIZE;
   if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
   if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
