@@ -28,7 +28,9 @@
 // buffer descriptor of each tile ends at the last valid key, so keys past Sk
 // read as zeros without any per-lane test.  LDS rows are 256 bytes, with the
 // 16-byte chunks XOR-swizzled by row so the MFMA operand reads are free of
-// bank conflicts.
+// bank conflicts on gfx950's 64-bank LDS (16 lanes per cycle for 16-byte
+// reads, 32 lanes per cycle for 8-byte reads): K chunk c of row r sits at
+// c ^ (r % 16), V chunk c of row r at c ^ 4(r % 4).
 //
 // Key order inside a 32-key block.  LDS K row i holds key
 // pi(i) = 16*(i/4 % 2) + 4*(i/8) + i%4, so that after the first product lane
@@ -180,7 +182,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
     const int kc = p ^ (r & 15);
     const int key = (r & 32) + key_of_k_row(r & 31);
     k_src[u] = (uint32_t)key * row_bytes + 16u * kc;
-    const int vc = p ^ (2 * (r & 7));
+    const int vc = p ^ (4 * (r & 3));
     v_src[u] = (uint32_t)r * row_bytes + 16u * vc;
   }
 
@@ -191,7 +193,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
   for (int ks = 0; ks < 8; ++ks) k_rd[ks] = 256u * l32 + 16u * ((2 * ks + grp) ^ (l32 & 15));
   // V (transposed reads): lane 16G + 4s + u reads keys 16(G/2) + 4half + s
   // (+32kb + 8hh), dims 32db + 16(G%2) + 4u .. +3, logical chunk
-  // 4db + 2(G%2) + u/2 at position chunk ^ (2 * (row % 8))
+  // 4db + 2(G%2) + u/2 at position chunk ^ (4 * (row % 4))
   uint32_t v_rd[4][2];
   {
     const int G = lane >> 4, sidx = (lane >> 2) & 3, u4 = lane & 3;
@@ -201,7 +203,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
       for (int half = 0; half < 2; ++half) {
         const int row = 16 * (G >> 1) + 4 * half + sidx;
         const int chunk = 4 * db + 2 * (G & 1) + (u4 >> 1);
-        v_rd[db][half] = 256u * row + 16u * (chunk ^ (2 * (row & 7))) + 8u * (u4 & 1);
+        v_rd[db][half] = 256u * row + 16u * (chunk ^ (4 * (row & 3))) + 8u * (u4 & 1);
       }
   }
 
