@@ -83,6 +83,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 // log2(e) / sqrt(128), rounded to fp32
 constexpr float kScaleLog2 = 0.12751743082459868f;
 // gfx9 buffer descriptor word 3: 32-bit data format, no swizzle, raw addressing
@@ -240,6 +242,15 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
         bf16x8 a = *(const bf16x8*)(kt + k_rd[ks] + 8192 * kb);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
+    // read K operands four MFMAs ahead of their use (the compiler otherwise
+    // issues each read just before its MFMA and the matrix core waits on LDS)
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
 
     // keys past Sk (only in the last tile) get a -Inf logit
     if (base + BN > Sk) {
@@ -307,6 +318,14 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hh], acc[db], 0, 0, 0);
         }
+    // V operands (two transposed reads each) four MFMAs ahead of their use
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
+#pragma unroll
+    for (int i = 0; i < 12; ++i) {
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
   // ---- main loop: two LDS stages, one barrier per tile ----
