@@ -111,6 +111,38 @@ def cpu_baseline(inp, target_s):
                       f"fp64 with 3 roundings), {dt:.2f} s"}
 
 
+def kernel_source_sha256() -> str:
+    import hashlib
+
+    path = os.path.join(ROOT, "bf16_forward_attention_amd", "csrc", "attn_fwd.hip")
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed FETCH_SIZE/WRITE_SIZE summary.
+
+    The summary (profiles/attn_fwd_traffic_<workload>.txt) records the two
+    counters per dispatch, the scale factors a plain copy of known size gave
+    them, and the SHA-256 of the kernel source they were taken on; a summary
+    of another kernel version gives None.
+    """
+    path = os.path.join(ROOT, "profiles", f"attn_fwd_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if "=" in line and not line.lstrip().startswith("#"):
+                k, v = line.split("=", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256") != kernel_source_sha256():
+        return None
+    fetch = float(kv["fetch_size_kib_per_launch"]) * float(kv["copy_fetch_scale"])
+    write = float(kv["write_size_kib_per_launch"]) * float(kv["copy_write_scale"])
+    return int(round((fetch + write) * 1024))
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -185,7 +217,8 @@ def main():
                                f"{mode.upper()}", "B": wl.B, "H": wl.H, "Sq": wl.Sq, "Sk": wl.Sk,
                    "head_dim": 128, "layout": wl.layout, "round_mode": mode},
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
-                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name),
                      "kernel": f"attn_fwd_kernel<{mode.upper()}>", "launch_ms_mean": round(float(per.mean()), 4),
                      "launch_ms_median": round(float(np.median(per)), 4)},
     }

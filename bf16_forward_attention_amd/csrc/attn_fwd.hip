@@ -7,9 +7,9 @@
 // the score matrix never leaves registers (the FlashAttention family the same
 // page places the design in, section "Memory-placement og mikroarkitektur").
 //
-// Work decomposition.  One workgroup of 4 wave64s owns BM = 128 query rows of
-// one (batch, head); each wave owns 32 of them.  Keys stream in tiles of
-// BN = 64.  Both products run on v_mfma_f32_32x32x16_bf16 in the transposed
+// Work decomposition.  One workgroup of 8 wave64s (two per SIMD) owns
+// BM = 256 query rows of one (batch, head); each wave owns 32 of them.  Keys
+// stream in tiles of BN = 64, shared through LDS by all eight waves.  Both products run on v_mfma_f32_32x32x16_bf16 in the transposed
 // orientation
 //     S^T (keys x queries)  = K   . Q^T      A = K tile (LDS), B = Q (VGPRs)
 //     O^T (dims x queries) += V^T . P^T      A = V tile read transposed (LDS), B = P (VGPRs)
@@ -24,7 +24,9 @@
 //
 // Data movement.  K and V tiles go from HBM straight into LDS with
 // buffer_load_dwordx4 ... lds (lane l of a load lands at 16*l past the
-// wave's LDS base), two stages deep, one workgroup barrier per tile.  The
+// wave's LDS base), four stages deep with loads issued three tiles ahead
+// (one tile of lead leaves the matrix cores waiting on load latency), one
+// workgroup barrier per tile.  The
 // buffer descriptor of each tile ends at the last valid key, so keys past Sk
 // read as zeros without any per-lane test.  LDS rows are 256 bytes, with the
 // 16-byte chunks XOR-swizzled by row so the MFMA operand reads are free of
@@ -59,17 +61,19 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <type_traits>
 
 #include "attn_fwd.h"
 
 namespace {
 
 constexpr int D = 128;
-constexpr int BM = 128;                // query rows per workgroup
+constexpr int BM = 256;                // query rows per workgroup
 constexpr int BN = 64;                 // keys per tile
-constexpr int NWAVES = BM / 32;        // 32 query rows per wave
+constexpr int NWAVES = BM / 32;        // 32 query rows per wave: 8 waves, two per SIMD
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS (16 KiB)
+constexpr int NSTAGE = 4;              // LDS stages: tiles are loaded three ahead
 constexpr float kRescaleLog2 = 8.0f;   // move the running maximum only past 2^8
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -123,18 +127,56 @@ __device__ __forceinline__ uint16_t round_to_bf16(float x) {
 // pi within a 32-key block: LDS row -> key
 __device__ __forceinline__ int key_of_k_row(int i) { return 16 * ((i >> 2) & 1) + 4 * (i >> 3) + (i & 3); }
 
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_records) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)num_records, kBufferWord3);
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// Raw buffer descriptor: 48-bit base, stride 0, num_records bytes, word 3.
+// All four words are wave-uniform (scalar registers).
+__device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_records) {
+  const uint64_t a = (uint64_t)base;
+  i32x4 r;
+  r[0] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int32_t)(uint32_t)(a >> 32) & 0xFFFF);
+  r[2] = __builtin_amdgcn_readfirstlane((int32_t)num_records);
+  r[3] = kBufferWord3;
+  return r;
+}
+
+// One direct-to-LDS load: 16 bytes per lane from rsrc + voffset land at
+// lds_base + 16 * lane.  Written as a single-instruction asm wrapper (plus
+// the M0 set-up and the one-cycle M0 hazard wait) so the compiler does not
+// track it as an LDS write: it would otherwise wait for every such load in
+// flight before each later LDS read, since it cannot tell which stage a load
+// fills.  The kernel orders these loads itself with s_waitcnt vmcnt and the
+// workgroup barrier (loads complete in order).  M0 is a reserved register
+// that the compiler itself sets right before each of its own uses.
+__device__ __forceinline__ void lds_dma_b128(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "memory");
+}
+
+// LDS address (offset within the workgroup's LDS) of a __shared__ pointer
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
 template <int MODE>
-__global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
+__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g) {
+  // one array per stage, so the compiler can tell the stages apart when it
+  // places waits for the direct-to-LDS loads
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t k_lds3[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t v_lds3[TILE_BYTES];
+  uint8_t* const k_st[NSTAGE] = {k_lds0, k_lds1, k_lds2, k_lds3};
+  uint8_t* const v_st[NSTAGE] = {v_lds0, v_lds1, v_lds2, v_lds3};
 
   // ---- workgroup -> (b, h, q-tile), keeping a head's q-tiles on one XCD ----
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that
@@ -172,14 +214,18 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
       qf[ks] = __builtin_bit_cast(bf16x8, w);
     }
   }
+  // Q must be in registers before the tile loop: the compiler cannot see the
+  // direct-to-LDS loads and would otherwise re-wait for Q inside the loop,
+  // draining the tile loads in flight with it.
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
 
-  // ---- direct-to-LDS load assignment: wave w issues loads j = 4w + u ----
+  // ---- direct-to-LDS load assignment: wave w issues loads j = 2w + u ----
   // Load j fills LDS rows 4j .. 4j+3 (1 KiB); lane l writes row 4j + l/16 at
   // 16-byte position l%16, which holds logical chunk (l%16) ^ swizzle(row).
-  uint32_t k_src[4], v_src[4];
+  uint32_t k_src[2], v_src[2];
 #pragma unroll
-  for (int u = 0; u < 4; ++u) {
-    const int r = 4 * (4 * wave + u) + (lane >> 4);
+  for (int u = 0; u < 2; ++u) {
+    const int r = 4 * (2 * wave + u) + (lane >> 4);
     const int p = lane & 15;
     const int kc = p ^ (r & 15);
     const int key = (r & 32) + key_of_k_row(r & 31);
@@ -209,17 +255,17 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
       }
   }
 
-  auto issue_loads = [&](int tile, uint8_t* kdst, uint8_t* vdst) {
+  auto issue_loads = [&](int tile, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
     const int base = tile * BN;
     const int valid = Sk - base < BN ? Sk - base : BN;
     const uint32_t nrec = (uint32_t)(valid - 1) * row_bytes + 256u;
-    const __amdgpu_buffer_rsrc_t rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
-    const __amdgpu_buffer_rsrc_t rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
+    const i32x4 rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
+    const i32x4 rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = 4 * wave + u;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (lds_void_t*)(kdst + 1024 * j), 16, k_src[u], 0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (lds_void_t*)(vdst + 1024 * j), 16, v_src[u], 0, 0, 0);
+    for (int u = 0; u < 2; ++u) {
+      const int j = 2 * wave + u;
+      lds_dma_b128(rk, __builtin_amdgcn_readfirstlane(lds_addr(kdst + 1024 * j)), k_src[u]);
+      lds_dma_b128(rv, __builtin_amdgcn_readfirstlane(lds_addr(vdst + 1024 * j)), v_src[u]);
     }
   };
 
@@ -231,7 +277,7 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
 
   const int n_tiles = (Sk + BN - 1) / BN;
 
-  auto compute_tile = [&](int t, const uint8_t* kt, const uint8_t* vt) {
+  auto compute_tile = [&](int t, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
     const int base = t * BN;
     // ---- S^T = K . Q^T for the two 32-key blocks ----
     f32x16 s[2] = {f32x16{}, f32x16{}};
@@ -328,19 +374,36 @@ __global__ __launch_bounds__(NTHREADS, 2) void attn_fwd_kernel(
     __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
   };
 
-  // ---- main loop: two LDS stages, one barrier per tile ----
+  // ---- main loop: four LDS stages, tiles loaded three ahead, one barrier per tile ----
+  // Tile t lives in stage t % 4.  Before computing tile t a wave waits until
+  // its own loads of tile t have landed (loads complete in order, so the
+  // four loads of each later tile in flight may remain outstanding), then
+  // the barrier makes every wave's loads visible and guarantees that stage
+  // (t+3) % 4, last read for tile t-1, is free for the loads of tile t+3.
+  auto step = [&](auto st_c, int t) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value;
+    if (t + 2 < n_tiles)
+      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tiles t+1 and t+2 may still be in flight
+    else if (t + 1 < n_tiles)
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+    else
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    __syncthreads();
+    if (t + 3 < n_tiles) issue_loads(t + 3, k_st[(ST + 3) % NSTAGE], v_st[(ST + 3) % NSTAGE]);
+    compute_tile(t, k_st[ST], v_st[ST]);
+  };
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   issue_loads(0, k_lds0, v_lds0);
-  for (int t = 0; t < n_tiles; t += 2) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's loads of tile t are in LDS
-    __syncthreads();                     // ... and every wave's; stage 1 is free again
-    if (t + 1 < n_tiles) issue_loads(t + 1, k_lds1, v_lds1);
-    compute_tile(t, k_lds0, v_lds0);
-    if (t + 1 < n_tiles) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
-      __syncthreads();                   // stage 0 is free again
-      if (t + 2 < n_tiles) issue_loads(t + 2, k_lds0, v_lds0);
-      compute_tile(t + 1, k_lds1, v_lds1);
-    }
+  if (n_tiles > 1) issue_loads(1, k_lds1, v_lds1);
+  if (n_tiles > 2) issue_loads(2, k_lds2, v_lds2);
+  for (int t = 0; t < n_tiles; t += 4) {
+    step(S0{}, t);
+    if (t + 1 < n_tiles) step(S1{}, t + 1);
+    if (t + 2 < n_tiles) step(S2{}, t + 2);
+    if (t + 3 < n_tiles) step(S3{}, t + 3);
   }
 
   // ---- epilogue: normalise, round, store this lane's query row ----
