@@ -9,8 +9,8 @@
 //
 // Work decomposition.  One workgroup of 8 wave64s (two per SIMD) owns
 // BM = 256 query rows of one (batch, head); each wave owns 32 of them.  Keys
-// stream in tiles of BN = 64, shared through LDS by all eight waves.  Both products run on v_mfma_f32_32x32x16_bf16 in the transposed
-// orientation
+// stream in tiles of BN = 64, shared through LDS by all eight waves.  Both
+// products run on v_mfma_f32_32x32x16_bf16 in the transposed orientation
 //     S^T (keys x queries)  = K   . Q^T      A = K tile (LDS), B = Q (VGPRs)
 //     O^T (dims x queries) += V^T . P^T      A = V tile read transposed (LDS), B = P (VGPRs)
 // so that every lane owns exactly one query row: the softmax row statistics
@@ -24,15 +24,23 @@
 //
 // Data movement.  K and V tiles go from HBM straight into LDS with
 // buffer_load_dwordx4 ... lds (lane l of a load lands at 16*l past the
-// wave's LDS base), four stages deep with loads issued three tiles ahead
-// (one tile of lead leaves the matrix cores waiting on load latency), one
-// workgroup barrier per tile.  The
-// buffer descriptor of each tile ends at the last valid key, so keys past Sk
-// read as zeros without any per-lane test.  LDS rows are 256 bytes, with the
-// 16-byte chunks XOR-swizzled by row so the MFMA operand reads are free of
-// bank conflicts on gfx950's 64-bank LDS (16 lanes per cycle for 16-byte
-// reads, 32 lanes per cycle for 8-byte reads): K chunk c of row r sits at
-// c ^ (r % 16), V chunk c of row r at c ^ 4(r % 4).
+// wave's LDS base), four stages deep with loads issued three tiles ahead,
+// one workgroup barrier per tile.  The buffer descriptor of each tile ends at
+// the last valid key, so keys past Sk read as zeros without any per-lane
+// test, and past the last tile the range is empty, so every iteration issues
+// the same loads and waits.  LDS rows are 256 bytes, with the 16-byte chunks
+// XOR-swizzled by row so the MFMA operand reads are free of bank conflicts
+// on gfx950's 64-bank LDS (16 lanes per cycle for 16-byte reads, 32 lanes
+// per cycle for 8-byte reads): K chunk c of row r sits at c ^ (r % 16), V
+// chunk c of row r at c ^ 4(r % 4).
+//
+// Schedule.  Each wave software-pipelines its tiles: iteration t computes
+// the K.Q logits of tile t+1 on the matrix core while the VALU turns the
+// logits of tile t into weights (exp2, row sum, bf16 pack), then the P.V
+// product of tile t while the VALU reduces the row maxima of tile t+1.  The
+// loads of tile t+3 are issued one instruction at a time between MFMAs.
+// When Sk is not a multiple of 64 the ragged last key tile is visited first,
+// so the one key mask happens before the loop.
 //
 // Key order inside a 32-key block.  LDS K row i holds key
 // pi(i) = 16*(i/4 % 2) + 4*(i/8) + i%4, so that after the first product lane
@@ -87,8 +95,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
 
-// instruction classes of __builtin_amdgcn_sched_group_barrier
-constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
+// the next tile's loads are issued one at a time after these MFMAs of each
+// half of an iteration
+constexpr int kHookAt0 = 1, kHookAt1 = 9;
 // log2(e) / sqrt(128), rounded to fp32
 constexpr float kScaleLog2 = 0.12751743082459868f;
 // gfx9 buffer descriptor word 3: 32-bit data format, no swizzle, raw addressing
@@ -255,17 +264,39 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
       }
   }
 
-  auto issue_loads = [&](int tile, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
-    const int base = tile * BN;
+  // Key tiles are visited in the order n-1, 0, 1, ..., n-2 when the last one
+  // is ragged, so that the only tile that needs a key mask is the first one,
+  // handled before the main loop (the order of the online softmax updates is
+  // free; only rounding depends on it).  Otherwise in the order 0 .. n-1.
+  const int n_tiles = (Sk + BN - 1) / BN;
+  const bool ragged = (Sk % BN) != 0;
+  // Buffer resources of the K and V rows of the seq-th visited tile.  Past
+  // the last tile the range is empty: those loads touch no memory (the
+  // hardware range check turns them into zeros), so every iteration issues
+  // the same number of loads and the load-count waits need no branches.
+  auto tile_rsrc = [&](int seq, i32x4& rk, i32x4& rv) __attribute__((always_inline)) {
+    const int tile = !ragged ? seq : (seq == 0 ? n_tiles - 1 : seq - 1);
+    const bool live = seq < n_tiles;
+    const int base = live ? tile * BN : 0;
     const int valid = Sk - base < BN ? Sk - base : BN;
-    const uint32_t nrec = (uint32_t)(valid - 1) * row_bytes + 256u;
-    const i32x4 rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
-    const i32x4 rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
+    const uint32_t nrec = live ? (uint32_t)(valid - 1) * row_bytes + 256u : 0u;
+    rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
+    rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
+  };
+  // this wave's two 1 KiB pieces of a K (or V) tile, straight into LDS
+  auto dma_k = [&](const i32x4& rk, uint8_t* kdst, int u) __attribute__((always_inline)) {
+    lds_dma_b128(rk, __builtin_amdgcn_readfirstlane(lds_addr(kdst + 1024 * (2 * wave + u))), k_src[u]);
+  };
+  auto dma_v = [&](const i32x4& rv, uint8_t* vdst, int u) __attribute__((always_inline)) {
+    lds_dma_b128(rv, __builtin_amdgcn_readfirstlane(lds_addr(vdst + 1024 * (2 * wave + u))), v_src[u]);
+  };
+  auto issue_loads = [&](int seq, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+    i32x4 rk, rv;
+    tile_rsrc(seq, rk, rv);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      const int j = 2 * wave + u;
-      lds_dma_b128(rk, __builtin_amdgcn_readfirstlane(lds_addr(kdst + 1024 * j)), k_src[u]);
-      lds_dma_b128(rv, __builtin_amdgcn_readfirstlane(lds_addr(vdst + 1024 * j)), v_src[u]);
+      dma_k(rk, kdst, u);
+      dma_v(rv, vdst, u);
     }
   };
 
@@ -275,52 +306,48 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   float m_run = -3.402823466e38f;
   float l_run = 0.0f;
 
-  const int n_tiles = (Sk + BN - 1) / BN;
+  f32x16 S[2][2];      // logits of two tiles: the one being turned into weights, the next one
+  bf16x8 pf[2][2];     // weights of the current tile, the B operand of P.V
+  float mx = 0.0f;     // row maximum of the next tile's logits
 
-  auto compute_tile = [&](int t, const uint8_t* kt, const uint8_t* vt) __attribute__((always_inline)) {
-    const int base = t * BN;
-    // ---- S^T = K . Q^T for the two 32-key blocks ----
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+  // S^T = K . Q^T for the two 32-key blocks of one tile (K stage kt)
+  auto qk = [&](f32x16 (&s)[2], const uint8_t* kt) __attribute__((always_inline)) {
+    s[0] = f32x16{};
+    s[1] = f32x16{};
 #pragma unroll
     for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        bf16x8 a = *(const bf16x8*)(kt + k_rd[ks] + 8192 * kb);
+        const bf16x8 a = *(const bf16x8*)(kt + k_rd[ks] + 8192 * kb);
         s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb], 0, 0, 0);
       }
-    // read K operands four MFMAs ahead of their use (the compiler otherwise
-    // issues each read just before its MFMA and the matrix core waits on LDS)
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
-    }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
-
-    // keys past Sk (only in the last tile) get a -Inf logit
-    if (base + BN > Sk) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int n = 0; n < 16; ++n)
-          if (base + 32 * kb + 16 * grp + n >= Sk) s[kb][n] = -__builtin_inff();
-    }
-
-    // ---- online softmax (base 2) ----
-    float mx = s[0][0];
+  };
+  // keys past Sk of key tile `tile` get a -Inf logit
+  auto mask_tail = [&](f32x16 (&s)[2], int tile) __attribute__((always_inline)) {
+    const int base = tile * BN;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int n = 0; n < 16; ++n) mx = fmaxf(mx, s[kb][n]);
-    mx = wave_half_max(mx);
-    // The candidate maximum is the scaled row maximum rounded up by at least
-    // half an ulp: then fma(s, c, -m) <= 0 for the maximal logit, its weight
-    // is exp2(<= 0) <= 1 and rounds to exactly 1 in bf16, so a row dominated
-    // by one key (or with a single key) returns that V row exactly in every
-    // mode.  (-Inf / NaN maxima give NaN here, which fmaxf ignores.)
-    const float mx_scaled = mx * kScaleLog2;
-    const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(mx_scaled), 0x1p-23f, mx_scaled));
+      for (int n = 0; n < 16; ++n)
+        if (base + 32 * kb + 16 * grp + n >= Sk) s[kb][n] = -__builtin_inff();
+  };
+  auto rowmax = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
+    float m = s[0][0];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int n = 0; n < 16; ++n) m = fmaxf(m, s[kb][n]);
+    mx = wave_half_max(m);
+  };
+  // Move the running maximum when some row's maximum grew past 2^8.  The
+  // candidate is the scaled row maximum rounded up by at least half an ulp:
+  // then fma(s, c, -m) <= 0 for the maximal logit, its weight exp2(<= 0) <= 1
+  // rounds to exactly 1 in bf16, so a row dominated by one key (or with a
+  // single key) returns that V row exactly in every mode.  (-Inf / NaN maxima
+  // give NaN here, which fmaxf ignores.)
+  auto rescale = [&]() __attribute__((always_inline)) {
+    const float ms = mx * kScaleLog2;
+    const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(ms), 0x1p-23f, ms));
     if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleLog2) != 0) {
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
@@ -328,82 +355,115 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] *= alpha;
     }
+  };
 
+  // Region A: K.Q of the next tile (sn, K stage kt) interleaved with the
+  // weights of the current one (sc): one MFMA, then one pair of weights.
+  // K operands are read four MFMAs ahead.
+  auto qk_weights = [&](f32x16 (&sn)[2], const f32x16 (&sc)[2], const uint8_t* kt, auto&& hook)
+                        __attribute__((always_inline)) {
+    sn[0] = f32x16{};
+    sn[1] = f32x16{};
+    bf16x8 ka[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ka[i] = *(const bf16x8*)(kt + k_rd[i >> 1] + 8192 * (i & 1));
     float psum = 0.0f;
-    bf16x8 pf[2][2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-#pragma unroll
-        for (int q2 = 0; q2 < 4; ++q2) {
-          const int n = 8 * hh + 2 * q2;
-          f32x2 p;
-          p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n], kScaleLog2, -m_run));
-          p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][n + 1], kScaleLog2, -m_run));
-          psum += p[0];
-          psum += p[1];
-          bf16x2 pb = __builtin_convertvector(p, bf16x2);
-          pf[kb][hh][2 * q2] = pb[0];
-          pf[kb][hh][2 * q2 + 1] = pb[1];
-        }
-      }
+    for (int i = 0; i < 16; ++i) {
+      if (i + 4 < 16) ka[i + 4] = *(const bf16x8*)(kt + k_rd[(i + 4) >> 1] + 8192 * ((i + 4) & 1));
+      sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i], qf[i >> 1], sn[i & 1], 0, 0, 0);
+      if (i == kHookAt0) hook(0);
+      if (i == kHookAt1) hook(1);
+      const int kb = i >> 3, hh = (i >> 2) & 1, q2 = i & 3, n = 8 * hh + 2 * q2;
+      f32x2 p;
+      p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][n], kScaleLog2, -m_run));
+      p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][n + 1], kScaleLog2, -m_run));
+      psum += p[0];
+      psum += p[1];
+      const bf16x2 pb = __builtin_convertvector(p, bf16x2);
+      pf[kb][hh][2 * q2] = pb[0];
+      pf[kb][hh][2 * q2 + 1] = pb[1];
     }
     l_run += psum;
-
-    // ---- O^T += V^T . P^T ----
+  };
+  // Region B: P.V of the current tile (V stage vt) interleaved with the row
+  // maxima of the next tile's logits: one MFMA, then two maxima.
+  auto pv_rowmax = [&](const uint8_t* vt, const f32x16 (&sn)[2], auto&& hook) __attribute__((always_inline)) {
+    bf16x8 va[16];
+    auto vread = [&](int i) __attribute__((always_inline)) {
+      const int kb = i >> 3, hh = (i >> 2) & 1, db = i & 3;
+      const uint8_t* vb = vt + 256 * (32 * kb + 8 * hh);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][0]));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][1]));
+      va[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    };
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int i = 0; i < 4; ++i) vread(i);
+    float m = sn[0][0];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          const uint8_t* vb = vt + 256 * (32 * kb + 8 * hh);
-          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][0]));
-          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][1]));
-          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kb][hh], acc[db], 0, 0, 0);
-        }
-    // V operands (two transposed reads each) four MFMAs ahead of their use
-    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 8, 0);
-#pragma unroll
-    for (int i = 0; i < 12; ++i) {
-      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+    for (int i = 0; i < 16; ++i) {
+      if (i + 4 < 16) vread(i + 4);
+      const int kb = i >> 3, hh = (i >> 2) & 1, db = i & 3;
+      acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf[kb][hh], acc[db], 0, 0, 0);
+      if (i == kHookAt0) hook(0);
+      if (i == kHookAt1) hook(1);
+      m = fmaxf(m, sn[i >> 3][2 * (i & 7)]);
+      m = fmaxf(m, sn[i >> 3][2 * (i & 7) + 1]);
     }
-    __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+    mx = wave_half_max(m);
   };
 
   // ---- main loop: four LDS stages, tiles loaded three ahead, one barrier per tile ----
-  // Tile t lives in stage t % 4.  Before computing tile t a wave waits until
-  // its own loads of tile t have landed (loads complete in order, so the
-  // four loads of each later tile in flight may remain outstanding), then
-  // the barrier makes every wave's loads visible and guarantees that stage
-  // (t+3) % 4, last read for tile t-1, is free for the loads of tile t+3.
-  auto step = [&](auto st_c, int t) __attribute__((always_inline)) {
-    constexpr int ST = decltype(st_c)::value;
-    if (t + 2 < n_tiles)
-      __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tiles t+1 and t+2 may still be in flight
-    else if (t + 1 < n_tiles)
-      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
-    else
-      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+  // Tile t lives in stage t % 4.  Iteration t turns the logits of tile t
+  // (S[t%2]) into weights while the matrix core computes the logits of tile
+  // t+1 (S[(t+1)%2]), then accumulates P.V of tile t while the VALU reduces
+  // the row maxima of tile t+1: each wave keeps its matrix core and its VALU
+  // busy at the same time.  Before the barrier of iteration t a wave waits
+  // for its own loads of tile t+1 (loads complete in order, so those of tile
+  // t+2 may remain in flight); the barrier makes every wave's loads visible
+  // and frees stage (t+3) % 4, last read in iteration t-1, for the loads of
+  // tile t+3.
+  auto body = [&](auto st_c, int t) __attribute__((always_inline)) {
+    constexpr int ST = decltype(st_c)::value, P = ST & 1;
+    rescale();
+    __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only the loads of tile t+2 may still be in flight
     __syncthreads();
-    if (t + 3 < n_tiles) issue_loads(t + 3, k_st[(ST + 3) % NSTAGE], v_st[(ST + 3) % NSTAGE]);
-    compute_tile(t, k_st[ST], v_st[ST]);
+    // loads of tile t+3, issued between MFMAs so that a full memory queue
+    // stalls this wave while its matrix work is under way
+    i32x4 rk, rv;
+    tile_rsrc(t + 3, rk, rv);
+    qk_weights(S[1 - P], S[P], k_st[(ST + 1) % NSTAGE],
+               [&](int u) __attribute__((always_inline)) { dma_k(rk, k_st[(ST + 3) % NSTAGE], u); });
+    pv_rowmax(v_st[ST], S[1 - P],
+              [&](int u) __attribute__((always_inline)) { dma_v(rv, v_st[(ST + 3) % NSTAGE], u); });
   };
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
   using S3 = std::integral_constant<int, 3>;
+
+  // prologue: tiles 0..2 of the visiting order in flight, logits and row
+  // maxima of the first (masked when it is the ragged one)
   issue_loads(0, k_lds0, v_lds0);
-  if (n_tiles > 1) issue_loads(1, k_lds1, v_lds1);
-  if (n_tiles > 2) issue_loads(2, k_lds2, v_lds2);
-  for (int t = 0; t < n_tiles; t += 4) {
-    step(S0{}, t);
-    if (t + 1 < n_tiles) step(S1{}, t + 1);
-    if (t + 2 < n_tiles) step(S2{}, t + 2);
-    if (t + 3 < n_tiles) step(S3{}, t + 3);
+  issue_loads(1, k_lds1, v_lds1);
+  issue_loads(2, k_lds2, v_lds2);
+  __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 has landed
+  __syncthreads();
+  qk(S[0], k_lds0);
+  if (ragged) mask_tail(S[0], n_tiles - 1);
+  rowmax(S[0]);
+
+  // In the iteration of the last tile the K.Q half reads a stage that holds
+  // no new tile; its logits are never used.
+  for (int t = 0;;) {
+    body(S0{}, t);
+    if (++t == n_tiles) break;
+    body(S1{}, t);
+    if (++t == n_tiles) break;
+    body(S2{}, t);
+    if (++t == n_tiles) break;
+    body(S3{}, t);
+    if (++t == n_tiles) break;
   }
 
   // ---- epilogue: normalise, round, store this lane's query row ----
