@@ -94,6 +94,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4_t;
+typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 
 // the next tile's loads are issued one at a time after these MFMAs of each
 // half of an iteration
@@ -176,16 +177,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g) {
   // one array per stage, so the compiler can tell the stages apart when it
   // places waits for the direct-to-LDS loads
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds2[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t k_lds3[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds2[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t v_lds3[TILE_BYTES];
-  uint8_t* const k_st[NSTAGE] = {k_lds0, k_lds1, k_lds2, k_lds3};
-  uint8_t* const v_st[NSTAGE] = {v_lds0, v_lds1, v_lds2, v_lds3};
+  // K stages in the lower 64 KiB, V stages in the upper 64 KiB
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
+  uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
+  uint8_t* const v_st[NSTAGE] = {lds + 4 * TILE_BYTES, lds + 5 * TILE_BYTES, lds + 6 * TILE_BYTES,
+                                 lds + 7 * TILE_BYTES};
 
   // ---- workgroup -> (b, h, q-tile), keeping a head's q-tiles on one XCD ----
   // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that
@@ -263,6 +259,19 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
         v_rd[db][half] = 256u * row + 16u * (chunk ^ (4 * (row & 3))) + 8u * (u4 & 1);
       }
   }
+
+  // The same offsets as LDS addresses in V stage 0, hidden from the compiler so
+  // that it keeps them in registers and folds the stage and block offsets
+  // (below 64 KiB) into each read's immediate offset field.
+  lds_u8_t* v_rd_lds[4][2];
+#pragma unroll
+  for (int db = 0; db < 4; ++db)
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+      uint32_t a = lds_addr(v_st[0]) + v_rd[db][half];
+      asm volatile("" : "+v"(a));
+      v_rd_lds[db][half] = (lds_u8_t*)(uintptr_t)a;
+    }
 
   // Key tiles are visited in the order n-1, 0, 1, ..., n-2 when the last one
   // is ragged, so that the only tile that needs a key mask is the first one,
@@ -388,13 +397,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   };
   // Region B: P.V of the current tile (V stage vt) interleaved with the row
   // maxima of the next tile's logits: one MFMA, then two maxima.
-  auto pv_rowmax = [&](const uint8_t* vt, const f32x16 (&sn)[2], auto&& hook) __attribute__((always_inline)) {
+  auto pv_rowmax = [&](int vstage, const f32x16 (&sn)[2], auto&& hook) __attribute__((always_inline)) {
     bf16x8 va[16];
     auto vread = [&](int i) __attribute__((always_inline)) {
       const int kb = i >> 3, hh = (i >> 2) & 1, db = i & 3;
-      const uint8_t* vb = vt + 256 * (32 * kb + 8 * hh);
-      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][0]));
-      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(vb + v_rd[db][1]));
+      const int off = vstage * TILE_BYTES + 256 * (32 * kb + 8 * hh);
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(v_rd_lds[db][0] + off));
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_t*)(v_rd_lds[db][1] + off));
       va[i] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     };
 #pragma unroll
@@ -434,7 +443,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     tile_rsrc(t + 3, rk, rv);
     qk_weights(S[1 - P], S[P], k_st[(ST + 1) % NSTAGE],
                [&](int u) __attribute__((always_inline)) { dma_k(rk, k_st[(ST + 3) % NSTAGE], u); });
-    pv_rowmax(v_st[ST], S[1 - P],
+    pv_rowmax(ST, S[1 - P],
               [&](int u) __attribute__((always_inline)) { dma_v(rv, v_st[(ST + 3) % NSTAGE], u); });
   };
   using S0 = std::integral_constant<int, 0>;
@@ -444,12 +453,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 
   // prologue: tiles 0..2 of the visiting order in flight, logits and row
   // maxima of the first (masked when it is the ragged one)
-  issue_loads(0, k_lds0, v_lds0);
-  issue_loads(1, k_lds1, v_lds1);
-  issue_loads(2, k_lds2, v_lds2);
+  issue_loads(0, k_st[0], v_st[0]);
+  issue_loads(1, k_st[1], v_st[1]);
+  issue_loads(2, k_st[2], v_st[2]);
   __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 has landed
   __syncthreads();
-  qk(S[0], k_lds0);
+  qk(S[0], k_st[0]);
   if (ragged) mask_tail(S[0], n_tiles - 1);
   rowmax(S[0]);
 
