@@ -1,8 +1,10 @@
 #!/usr/bin/env python3
 """Benchmark of the fused bf16 forward attention on one MI355X.
 
-A step is one call of attn_fwd_bf16 over the whole workload (every query row
-of every head), inputs resident in HBM.  Default workload: self-attention
+A step is one call of the library over the whole workload (every query row of
+every head), inputs resident in HBM: attn_fwd_bf16_ws with a preallocated
+workspace when the shape splits its key ranges (then the step is both of its
+kernels), attn_fwd_bf16 otherwise.  Default workload: self-attention
 B=4, H=16, Sq=Sk=8192, d=128, BSHD, RTNE.  Prints one JSON line:
 
   value      forward TFLOP/s, 4*B*H*Sq*Sk*128 FLOPs / mean step time
@@ -47,6 +49,7 @@ def parse():
     p.add_argument("--workload", default="self8k")
     p.add_argument("--mode", default=None, help="rounding mode (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-split", action="store_true", help="always call attn_fwd_bf16 (single pass)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for the sample")
     p.add_argument("--parity-rows", type=int, default=256)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -166,11 +169,24 @@ def main():
     q, k, v = t(inp.q), t(inp.k), t(inp.v)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
+    ws_bytes = 0 if args.no_split else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
-              attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode], stream.cuda_stream)
+              attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
+    if ws_bytes > 0:
+        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan(
+            wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64), torch.cuda.get_device_properties(dev).multi_processor_count)
+        entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
+                 f"{tps} tiles, {ws_bytes} B workspace")
+    else:
+        entry = "attn_fwd_bf16"
+    log(f"[bench] entry point: {entry}")
 
     def step():
-        st = attn.attn_fwd_bf16(*args_c)
+        if ws_bytes > 0:
+            st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+        else:
+            st = attn.attn_fwd_bf16(*args_c, stream.cuda_stream)
         if st != 0:
             raise attn.AttnError(st)
 
@@ -216,10 +232,12 @@ def main():
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} Sq={wl.Sq} Sk={wl.Sk} d=128 {wl.layout.upper()} "
                                f"{mode.upper()}", "B": wl.B, "H": wl.H, "Sq": wl.Sq, "Sk": wl.Sk,
                    "head_dim": 128, "layout": wl.layout, "round_mode": mode},
+        "entry_point": entry,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name),
-                     "kernel": f"attn_fwd_kernel<{mode.upper()}>", "launch_ms_mean": round(float(per.mean()), 4),
+                     "kernel": f"attn_fwd_kernel<{mode.upper()}>" + (" + attn_merge_kernel" if ws_bytes else ""),
+                     "launch_ms_mean": round(float(per.mean()), 4),
                      "launch_ms_median": round(float(np.median(per)), 4)},
     }
     if not args.no_cpu_baseline:

@@ -5,7 +5,10 @@ only, every step of the computation runs in the HIP library
 ``libattn_fwd.so``.  PyTorch is used for device memory and streams.
 
     attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
-    attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne") -> torch.Tensor
+    attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
+    attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
+    attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
+    attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True) -> torch.Tensor
 """
 from __future__ import annotations
 
@@ -13,7 +16,8 @@ import ctypes
 import os
 
 __all__ = [
-    "attn_fwd_bf16", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
+    "attn_fwd_bf16", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_split_plan",
+    "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
     "AttnError", "LAYOUTS", "ROUND_MODES", "library_path", "load_library",
 ]
 
@@ -50,6 +54,13 @@ def load_library():
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
         lib.attn_fwd_bf16.restype = ctypes.c_int
+        lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
+                                         vp]
+        lib.attn_fwd_bf16_ws.restype = ctypes.c_int
+        lib.attn_fwd_bf16_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.POINTER(i64)]
+        lib.attn_fwd_bf16_workspace_size.restype = ctypes.c_int
+        lib.attn_fwd_bf16_split_plan.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
+        lib.attn_fwd_bf16_split_plan.restype = ctypes.c_int
         lib.attn_fwd_bf16_strerror.argtypes = [ctypes.c_int]
         lib.attn_fwd_bf16_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_bf16_abi_version.argtypes = []
@@ -62,6 +73,31 @@ def attn_fwd_bf16(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: i
                   layout: int, round_mode: int, stream: int) -> int:
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream)
+
+
+def attn_fwd_bf16_ws(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int, layout: int,
+                     round_mode: int, workspace: int, workspace_bytes: int, stream: int) -> int:
+    """The key-range-splitting C entry point; returns the status code."""
+    return load_library().attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, workspace,
+                                           workspace_bytes, stream)
+
+
+def attn_fwd_bf16_workspace_size(B: int, H: int, Sq: int, Sk: int) -> int:
+    """Workspace bytes attn_fwd_bf16_ws needs on the current device (raises AttnError)."""
+    out = ctypes.c_int64(0)
+    status = load_library().attn_fwd_bf16_workspace_size(B, H, Sq, Sk, ctypes.byref(out))
+    if status != 0:
+        raise AttnError(status)
+    return out.value
+
+
+def attn_fwd_bf16_split_plan(n_work: int, n_tiles: int, n_cu: int):
+    """(items run whole, items split, ranges per split item, tiles per range)."""
+    out = (ctypes.c_int64 * 4)()
+    status = load_library().attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu, out)
+    if status != 0:
+        raise AttnError(status)
+    return tuple(out)
 
 
 def attn_fwd_bf16_strerror(status: int) -> str:
@@ -86,12 +122,15 @@ def _dims(q, k, layout: str):
     return B, H, Sq, Sk
 
 
-def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None):
+def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None,
+             split: bool = True):
     """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
 
     ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H,128] for "bshd", or
     [B,H,S,128] for "bhsd"; all contiguous bf16 on one device.  Enqueued on
-    ``stream`` (default: torch's current stream on that device).
+    ``stream`` (default: torch's current stream on that device).  With
+    ``split`` the key range may be split (attn_fwd_bf16_ws, workspace from
+    torch); without, the single-pass attn_fwd_bf16.
     """
     import torch
 
@@ -112,8 +151,16 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        status = attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
-                               LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
+        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split else 0
+        if ws_bytes > 0:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            status = attn_fwd_bf16_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
+                                      LAYOUTS[layout], ROUND_MODES[round_mode], ws.data_ptr(), ws_bytes,
+                                      s.cuda_stream)
+            ws.record_stream(s)
+        else:
+            status = attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
+                                   LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
     if status != 0:
         raise AttnError(status)
     return out

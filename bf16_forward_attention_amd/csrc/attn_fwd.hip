@@ -89,6 +89,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -111,6 +112,21 @@ struct Geometry {
   int64_t k_head;
   int64_t q_batch; // element offset of batch b
   int64_t k_batch;
+};
+
+// Work items are (b, h, q-tile) in row-major order.  Items [0, n_whole) run
+// whole, one workgroup each; every later item runs as `splits` workgroups,
+// each over `tiles_per_split` consecutive key tiles of the visiting order,
+// leaving its unnormalised output rows (fp32), the running maximum m (base-2
+// scaled logits) and row sum l of its key range in the workspace for
+// attn_merge_kernel.  Partial slot r (= workgroup id - n_whole) holds
+//     part[(r * BM + row) * D + c],  ml[(r * BM + row) * 2 + {0: m, 1: l}].
+struct Split {
+  int n_whole;
+  int splits;
+  int tiles_per_split;
+  float* part;
+  float* ml;
 };
 
 // Combine a per-lane value with the one held 32 lanes away (the other half of
@@ -174,7 +190,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 template <int MODE>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g) {
+    uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp) {
   // one array per stage, so the compiler can tell the stages apart when it
   // places waits for the direct-to-LDS loads
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
@@ -183,14 +199,23 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   uint8_t* const v_st[NSTAGE] = {lds + 4 * TILE_BYTES, lds + 5 * TILE_BYTES, lds + 6 * TILE_BYTES,
                                  lds + 7 * TILE_BYTES};
 
-  // ---- workgroup -> (b, h, q-tile), keeping a head's q-tiles on one XCD ----
-  // Workgroups are dispatched round-robin over the 8 XCDs; renumber so that
-  // XCD x receives a contiguous range of logical work items.
-  const int nwg = gridDim.x;
+  // ---- workgroup -> (b, h, q-tile) and key-tile range ----
+  // Whole items: workgroups are dispatched round-robin over the 8 XCDs;
+  // renumber so that XCD x receives a contiguous range of logical work items
+  // (a head's q-tiles share one XCD's L2).  Split items follow in id order.
+  const int n_tiles_all = (Sk + BN - 1) / BN;
   const int id = blockIdx.x;
-  const int xcd = id & 7, local = id >> 3;
-  const int per = nwg >> 3, rem = nwg & 7;
-  const int work = xcd * per + (xcd < rem ? xcd : rem) + local;
+  int work, t_begin = 0, t_end = n_tiles_all, slot = -1;
+  if (id < sp.n_whole) {
+    const int xcd = id & 7, local = id >> 3;
+    const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
+    work = xcd * per + (xcd < rem ? xcd : rem) + local;
+  } else {
+    slot = id - sp.n_whole;
+    work = sp.n_whole + slot / sp.splits;
+    t_begin = (slot % sp.splits) * sp.tiles_per_split;
+    t_end = t_begin + sp.tiles_per_split < n_tiles_all ? t_begin + sp.tiles_per_split : n_tiles_all;
+  }
   const int qt = work % n_qtiles;
   const int bh = work / n_qtiles;
   const int h = bh % H, b = bh / H;
@@ -277,15 +302,18 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // is ragged, so that the only tile that needs a key mask is the first one,
   // handled before the main loop (the order of the online softmax updates is
   // free; only rounding depends on it).  Otherwise in the order 0 .. n-1.
-  const int n_tiles = (Sk + BN - 1) / BN;
+  // This workgroup visits positions t_begin .. t_end-1 of that order; loop
+  // indices below count from t_begin.
+  const int n_tiles = t_end - t_begin;
   const bool ragged = (Sk % BN) != 0;
   // Buffer resources of the K and V rows of the seq-th visited tile.  Past
   // the last tile the range is empty: those loads touch no memory (the
   // hardware range check turns them into zeros), so every iteration issues
   // the same number of loads and the load-count waits need no branches.
-  auto tile_rsrc = [&](int seq, i32x4& rk, i32x4& rv) __attribute__((always_inline)) {
-    const int tile = !ragged ? seq : (seq == 0 ? n_tiles - 1 : seq - 1);
-    const bool live = seq < n_tiles;
+  auto tile_rsrc = [&](int t, i32x4& rk, i32x4& rv) __attribute__((always_inline)) {
+    const int seq = t_begin + t;
+    const int tile = !ragged ? seq : (seq == 0 ? n_tiles_all - 1 : seq - 1);
+    const bool live = t < n_tiles;
     const int base = live ? tile * BN : 0;
     const int valid = Sk - base < BN ? Sk - base : BN;
     const uint32_t nrec = live ? (uint32_t)(valid - 1) * row_bytes + 256u : 0u;
@@ -459,7 +487,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 has landed
   __syncthreads();
   qk(S[0], k_st[0]);
-  if (ragged) mask_tail(S[0], n_tiles - 1);
+  if (ragged && t_begin == 0) mask_tail(S[0], n_tiles_all - 1);
   rowmax(S[0]);
 
   // In the iteration of the last tile the K.Q half reads a stage that holds
@@ -475,8 +503,22 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     if (++t == n_tiles) break;
   }
 
-  // ---- epilogue: normalise, round, store this lane's query row ----
+  // ---- epilogue ----
   const float l_tot = wave_half_sum(l_run);
+  if (slot >= 0) {
+    // partial result of a key range: unnormalised rows, m and l
+    const int row = wave * 32 + l32;
+    float* prow = sp.part + ((int64_t)slot * BM + row) * D + 4 * grp;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        *(f32x4*)(prow + 32 * db + 8 * r) =
+            f32x4{acc[db][4 * r], acc[db][4 * r + 1], acc[db][4 * r + 2], acc[db][4 * r + 3]};
+    if (grp == 0) *(f32x2*)(sp.ml + ((int64_t)slot * BM + row) * 2) = f32x2{m_run, l_tot};
+    return;
+  }
+  // normalise, round, store this lane's query row
   const float inv_l = 1.0f / l_tot;
   if (qrow < Sq) {
     uint16_t* dst = Oh + (int64_t)qrow * g.q_row + 4 * grp;
@@ -493,24 +535,70 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   }
 }
 
+// Combines the key-range partials of the split work items: per query row,
+// M = max_s m_s, w_s = 2^(m_s - M), O = (sum_s w_s o_s) * (1 / sum_s w_s l_s),
+// summed in split order, then the one rounding to bf16.  One thread per
+// (item, row, 4 dims).  A split whose logits were all -Inf has m_s = -FLT_MAX
+// and contributes nothing; a row with no finite logit at all gives 0 * Inf =
+// NaN, as in the whole-row kernel.
+template <int MODE>
+__global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, int H, int Sq, int n_qtiles,
+                                                         Geometry g, Split sp, int n_split_items) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= (int64_t)n_split_items * BM * (D / 4)) return;
+  const int c4 = (int)(gid % (D / 4));
+  const int row = (int)((gid / (D / 4)) % BM);
+  const int item = (int)(gid / ((D / 4) * BM));
+  const int work = sp.n_whole + item;
+  const int qt = work % n_qtiles, bh = work / n_qtiles;
+  const int h = bh % H, b = bh / H;
+  const int qrow = qt * BM + row;
+  if (qrow >= Sq) return;
+  const int64_t slot0 = (int64_t)item * sp.splits;
+  float mmax = -3.402823466e38f;
+  for (int s = 0; s < sp.splits; ++s) mmax = fmaxf(mmax, sp.ml[((slot0 + s) * BM + row) * 2]);
+  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f;
+  for (int s = 0; s < sp.splits; ++s) {
+    const f32x2 ml = *(const f32x2*)(sp.ml + ((slot0 + s) * BM + row) * 2);
+    const float w = __builtin_amdgcn_exp2f(ml[0] - mmax);
+    const f32x4 o = *(const f32x4*)(sp.part + ((slot0 + s) * BM + row) * D + 4 * c4);
+    num += w * o;
+    den += w * ml[1];
+  }
+  const float inv = 1.0f / den;
+  uint16_t* dst = O + b * g.q_batch + h * g.q_head + (int64_t)qrow * g.q_row + 4 * c4;
+  const uint32_t lo = round_to_bf16<MODE>(num[0] * inv) | ((uint32_t)round_to_bf16<MODE>(num[1] * inv) << 16);
+  const uint32_t hi = round_to_bf16<MODE>(num[2] * inv) | ((uint32_t)round_to_bf16<MODE>(num[3] * inv) << 16);
+  *(u32x2*)dst = u32x2{lo, hi};
+}
+
 // ---------------------------------------------------------------------------
 // host side
 // ---------------------------------------------------------------------------
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
+std::atomic<int> g_cu_count[kMaxDevices];    // 0 unknown
 
-int check_device() {
+int check_device(int* n_cu) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
   if (dev < kMaxDevices) {
-    int st = g_arch_state[dev].load(std::memory_order_acquire);
-    if (st == 1) return ATTN_OK;
+    const int st = g_arch_state[dev].load(std::memory_order_acquire);
     if (st == 2) return ATTN_ERR_DEVICE;
+    if (st == 1) {
+      *n_cu = g_cu_count[dev].load(std::memory_order_relaxed);
+      return ATTN_OK;
+    }
   }
   hipDeviceProp_t prop;
   if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return ATTN_ERR_DEVICE;
-  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
-  if (dev < kMaxDevices) g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 && prop.multiProcessorCount > 0;
+  *n_cu = prop.multiProcessorCount;
+  if (dev < kMaxDevices) {
+    g_cu_count[dev].store(prop.multiProcessorCount, std::memory_order_relaxed);
+    g_arch_state[dev].store(ok ? 1 : 2, std::memory_order_release);
+  }
   return ok ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
@@ -521,30 +609,64 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
 }
 
-}  // namespace
+// Split plan for n_work items of n_tiles key tiles on n_cu compute units
+// (one workgroup per CU at a time).  When the items do not fill the last
+// round of CUs, the items of that round run as several key ranges each, so
+// the round holds as many workgroups as there are CUs; a range holds at
+// least kMinSplitTiles tiles.
+constexpr int kMinSplitTiles = 4;
+struct Plan {
+  int64_t n_whole, n_split_items, splits, tiles_per_split;
+};
+Plan make_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu) {
+  Plan p{n_work, 0, 1, n_tiles};
+  if (n_cu < 1 || n_work % n_cu == 0) return p;
+  const int64_t n_tail = n_work % n_cu;
+  int64_t splits = n_cu / n_tail;
+  if (splits > n_tiles / kMinSplitTiles) splits = n_tiles / kMinSplitTiles;
+  if (splits < 2) return p;
+  const int64_t tps = (n_tiles + splits - 1) / splits;
+  splits = (n_tiles + tps - 1) / tps;  // every range non-empty
+  if (splits < 2) return p;
+  p.n_whole = n_work - n_tail;
+  p.n_split_items = n_tail;
+  p.splits = splits;
+  p.tiles_per_split = tps;
+  return p;
+}
+int64_t plan_workspace_bytes(const Plan& p) {
+  return p.n_split_items * p.splits * BM * (D + 2) * (int64_t)sizeof(float);
+}
 
-extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
-                             int64_t Sq, int64_t Sk, int layout, int round_mode, void* stream) {
+struct Problem {
+  int64_t bytes_q, bytes_k, n_work, n_qtiles, n_tiles;
+};
+// argument checks shared by the entry points (no HIP calls)
+int check_args(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t H, int64_t Sq,
+               int64_t Sk, int layout, int round_mode, Problem* pb) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
   if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SIZE;
-  int64_t bh, nq, nk, bytes_q, bytes_k;
-  if (!mul_ok(B, H, &bh) || !mul_ok(bh, Sq, &nq) || !mul_ok(nq, 2 * D, &bytes_q) || !mul_ok(bh, Sk, &nk) ||
-      !mul_ok(nk, 2 * D, &bytes_k))
+  int64_t bh, nq, nk;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, Sq, &nq) || !mul_ok(nq, 2 * D, &pb->bytes_q) || !mul_ok(bh, Sk, &nk) ||
+      !mul_ok(nk, 2 * D, &pb->bytes_k))
     return ATTN_ERR_SIZE;
-  const int64_t n_qtiles = (Sq + BM - 1) / BM;
-  int64_t n_wg;
+  pb->n_qtiles = (Sq + BM - 1) / BM;
+  pb->n_tiles = (Sk + BN - 1) / BN;
   // one 64-key tile of rows must be addressable by 32-bit buffer offsets
-  if (!mul_ok(bh, n_qtiles, &n_wg) || n_wg > INT32_MAX || Sq > INT32_MAX || Sk > INT32_MAX || H > (1 << 20))
+  if (!mul_ok(bh, pb->n_qtiles, &pb->n_work) || pb->n_work > INT32_MAX - 65536 || Sq > INT32_MAX ||
+      Sk > INT32_MAX || H > (1 << 20))
     return ATTN_ERR_SIZE;
   if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
   if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
     return ATTN_ERR_ROUND;
   if (((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) return ATTN_ERR_ALIGN;
-  if (overlaps(o, bytes_q, q, bytes_q) || overlaps(o, bytes_q, k, bytes_k) || overlaps(o, bytes_q, v, bytes_k))
+  if (overlaps(o, pb->bytes_q, q, pb->bytes_q) || overlaps(o, pb->bytes_q, k, pb->bytes_k) ||
+      overlaps(o, pb->bytes_q, v, pb->bytes_k))
     return ATTN_ERR_ALIAS;
-  const int dev_status = check_device();
-  if (dev_status != ATTN_OK) return dev_status;
+  return ATTN_OK;
+}
 
+Geometry make_geometry(int64_t H, int64_t Sq, int64_t Sk, int layout) {
   Geometry g;
   if (layout == ATTN_LAYOUT_BSHD) {
     g.q_row = H * D;
@@ -561,38 +683,123 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
     g.q_batch = H * Sq * D;
     g.k_batch = H * Sk * D;
   }
-  const dim3 grid((unsigned)n_wg), block(NTHREADS);
-  hipStream_t s = (hipStream_t)stream;
+  return g;
+}
+
+template <int MODE>
+void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
+            int n_qtiles, const Geometry& g, const Split& sp, int64_t n_wg, int n_split_items, hipStream_t s) {
+  hipLaunchKernelGGL(attn_fwd_kernel<MODE>, dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H, Sq, Sk,
+                     n_qtiles, g, sp);
+  if (n_split_items > 0) {
+    const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
+    hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
+                       Sq, n_qtiles, g, sp, n_split_items);
+  }
+}
+
+int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t Sq, int64_t Sk, int layout,
+        int round_mode, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
+  const Geometry g = make_geometry(H, Sq, Sk, layout);
+  Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
+  if (plan.n_split_items > 0) {
+    sp.part = (float*)workspace;
+    sp.ml = sp.part + plan.n_split_items * plan.splits * BM * D;
+  }
+  const int64_t n_wg = plan.n_whole + plan.n_split_items * plan.splits;
   const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
   uint16_t* oo = (uint16_t*)o;
+  hipStream_t s = (hipStream_t)stream;
+  const int nsi = (int)plan.n_split_items;
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
-      hipLaunchKernelGGL(attn_fwd_kernel<ATTN_ROUND_RTNE>, grid, block, 0, s, qq, kk, vv, oo, (int)H, (int)Sq,
-                         (int)Sk, (int)n_qtiles, g);
+      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
       break;
     case ATTN_ROUND_RTNA:
-      hipLaunchKernelGGL(attn_fwd_kernel<ATTN_ROUND_RTNA>, grid, block, 0, s, qq, kk, vv, oo, (int)H, (int)Sq,
-                         (int)Sk, (int)n_qtiles, g);
+      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
       break;
     default:
-      hipLaunchKernelGGL(attn_fwd_kernel<ATTN_ROUND_RTZ>, grid, block, 0, s, qq, kk, vv, oo, (int)H, (int)Sq,
-                         (int)Sk, (int)n_qtiles, g);
+      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
       break;
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
+}  // namespace
+
+extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                             int64_t Sq, int64_t Sk, int layout, int round_mode, void* stream) {
+  Problem pb;
+  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  if (st != ATTN_OK) return st;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
+  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, pb, whole, nullptr, stream);
+}
+
+extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {
+  if (!out4) return ATTN_ERR_NULL;
+  if (n_work < 1 || n_tiles < 1 || n_cu < 1) return ATTN_ERR_SIZE;
+  const Plan p = make_plan(n_work, n_tiles, n_cu);
+  out4[0] = p.n_whole;
+  out4[1] = p.n_split_items;
+  out4[2] = p.splits;
+  out4[3] = p.tiles_per_split;
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_bf16_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULL;
+  *bytes = 0;
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SIZE;
+  int64_t bh, n_work;
+  const int64_t n_qtiles = (Sq + BM - 1) / BM;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, n_qtiles, &n_work) || n_work > INT32_MAX - 65536 || Sk > INT32_MAX)
+    return ATTN_ERR_SIZE;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  *bytes = plan_workspace_bytes(make_plan(n_work, (Sk + BN - 1) / BN, n_cu));
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                                int64_t Sq, int64_t Sk, int layout, int round_mode, void* workspace,
+                                int64_t workspace_bytes, void* stream) {
+  Problem pb;
+  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  if (st != ATTN_OK) return st;
+  if (workspace_bytes < 0) return ATTN_ERR_SIZE;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  Plan plan = make_plan(pb.n_work, pb.n_tiles, n_cu);
+  const int64_t need = plan_workspace_bytes(plan);
+  if (need > 0) {
+    if (!workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15) return ATTN_ERR_ALIGN;
+    if (overlaps(workspace, need, q, pb.bytes_q) || overlaps(workspace, need, k, pb.bytes_k) ||
+        overlaps(workspace, need, v, pb.bytes_k) || overlaps(workspace, need, o, pb.bytes_q))
+      return ATTN_ERR_ALIAS;
+  }
+  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, pb, plan, workspace, stream);
+}
+
 extern "C" const char* attn_fwd_bf16_strerror(int status) {
   switch (status) {
     case ATTN_OK: return "success";
-    case ATTN_ERR_NULL: return "a tensor pointer is NULL";
+    case ATTN_ERR_NULL: return "a tensor or workspace pointer is NULL";
     case ATTN_ERR_SIZE: return "B, H, Sq and Sk must be >= 1 and the problem must fit the index types";
     case ATTN_ERR_LAYOUT: return "layout must be ATTN_LAYOUT_BSHD or ATTN_LAYOUT_BHSD";
     case ATTN_ERR_ROUND: return "round_mode must be ATTN_ROUND_RTNE, ATTN_ROUND_RTNA or ATTN_ROUND_RTZ";
-    case ATTN_ERR_ALIGN: return "q, k, v and o must be 16-byte aligned";
-    case ATTN_ERR_ALIAS: return "o overlaps q, k or v";
+    case ATTN_ERR_ALIGN: return "q, k, v, o and the workspace must be 16-byte aligned";
+    case ATTN_ERR_ALIAS: return "o or the workspace overlaps another buffer";
     case ATTN_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X) or cannot be queried";
     case ATTN_ERR_HIP: return "the HIP kernel launch failed";
+    case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_bf16_workspace_size reports";
     default: return "unknown status";
   }
 }

@@ -29,9 +29,10 @@
  *     BHSD: Q/O [B, H, Sq, 128], K/V [B, H, Sk, 128];
  *           (b, h, s, c) at ((b*H + h)*S + s)*128 + c
  *
- * Ownership: the caller owns every buffer.  The library allocates nothing on
- * the device, never synchronises, and keeps no state beyond a once-filled
- * per-device architecture cache; calls are thread-safe.
+ * Ownership: the caller owns every buffer, including the workspace of
+ * attn_fwd_bf16_ws.  The library allocates nothing on the device, never
+ * synchronises, and keeps no state beyond a once-filled per-device cache of
+ * the architecture and compute-unit count; calls are thread-safe.
  */
 #ifndef ATTN_FWD_H
 #define ATTN_FWD_H
@@ -42,7 +43,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 1
+#define ATTN_FWD_ABI_VERSION 2
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -65,7 +66,8 @@ typedef enum {
     ATTN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned */
     ATTN_ERR_ALIAS = 6,  /* o overlaps q, k or v */
     ATTN_ERR_DEVICE = 7, /* the current device is not gfx950, or cannot be queried */
-    ATTN_ERR_HIP = 8     /* the kernel launch failed */
+    ATTN_ERR_HIP = 8,    /* the kernel launch failed */
+    ATTN_ERR_WORKSPACE = 9 /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
 } attn_status_t;
 
 /*
@@ -89,6 +91,57 @@ typedef enum {
 int attn_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                   int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                   int layout, int round_mode, void *stream);
+
+/*
+ * attn_fwd_bf16_ws -- the same operation, allowed to split the key range.
+ *
+ * Each workgroup of the kernel owns 256 query rows of one (batch, head) and
+ * the machine runs one per compute unit at a time.  When B*H*ceil(Sq/256)
+ * leaves the last round of compute units partly idle (a short Sq against a
+ * long Sk, few heads), the work items of that round run as several
+ * workgroups over consecutive key ranges each, and a second kernel merges
+ * their partial results by the same max-shifted sums the online softmax uses
+ * (the split-over-keys arrangement the FlashAttention family uses for long
+ * keys), then rounds once in the requested mode.
+ *
+ *   workspace       : device memory of at least the size
+ *                     attn_fwd_bf16_workspace_size reports for this shape,
+ *                     16-byte aligned, not overlapping q, k, v or o; it holds
+ *                     fp32 partial rows and is only read by the same call.
+ *                     May be NULL when that size is 0.
+ *   workspace_bytes : its size in bytes.
+ *   other arguments : as attn_fwd_bf16.
+ *
+ * Same status codes as attn_fwd_bf16, plus ATTN_ERR_NULL (workspace NULL but
+ * needed), ATTN_ERR_WORKSPACE (too small), ATTN_ERR_ALIGN / ATTN_ERR_ALIAS for
+ * the workspace.  When the reported size is 0 this is exactly attn_fwd_bf16.
+ * A split changes the order of the fp32 sums, so its results can differ from
+ * attn_fwd_bf16's in the last bits (both are within the same tolerance of the
+ * exact result); for a given shape and device they are deterministic.  Calls
+ * that share a workspace must be ordered on one stream.
+ */
+int attn_fwd_bf16_ws(const void *q, const void *k, const void *v, void *o,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                     int layout, int round_mode, void *workspace,
+                     int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs
+ * for this shape on the current device (0: it will not split).  Writes
+ * *bytes; returns ATTN_ERR_NULL, ATTN_ERR_SIZE or ATTN_ERR_DEVICE like the
+ * other calls.  At most 256 (compute units) x 256 rows x 130 floats.
+ */
+int attn_fwd_bf16_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                                 int64_t *bytes);
+
+/*
+ * attn_fwd_bf16_split_plan -- the split decision, as a pure function for
+ * testing: n_work items of n_tiles 64-key tiles on n_cu compute units.
+ * out4 = {items run whole, items split, ranges per split item, tiles per
+ * range}.  Returns ATTN_ERR_NULL or ATTN_ERR_SIZE (any argument < 1).
+ */
+int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu,
+                             int64_t *out4);
 
 /* Static description of a status code (never NULL). */
 const char *attn_fwd_bf16_strerror(int status);

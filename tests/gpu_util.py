@@ -42,6 +42,27 @@ def launch(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
         raise attn.AttnError(st)
 
 
+def launch_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
+              stream: torch.cuda.Stream | None = None) -> int:
+    """Call attn_fwd_bf16_ws (key ranges split when it pays) with a torch-allocated
+    workspace of the size the library asks for; returns that size."""
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Sk = k.shape[1]
+    else:
+        B, H, Sq, _ = q.shape
+        Sk = k.shape[2]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    nbytes = attn.attn_fwd_bf16_workspace_size(B, H, Sq, Sk)
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = attn.attn_fwd_bf16_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Sq, Sk,
+                               attn.LAYOUTS[layout], attn.ROUND_MODES[mode], ws.data_ptr(), nbytes, s.cuda_stream)
+    if st != 0:
+        raise attn.AttnError(st)
+    torch.cuda.synchronize()
+    return nbytes
+
+
 class Dev:
     """Device copies of one Inputs bundle."""
 
@@ -51,14 +72,17 @@ class Dev:
         self.q, self.k, self.v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
         self.o = torch.empty_like(self.q)
 
-    def run(self, mode: str) -> np.ndarray:
-        """Output bits in the stored layout."""
-        launch(self.q, self.k, self.v, self.o, self.layout, mode)
+    def run(self, mode: str, split: bool = False) -> np.ndarray:
+        """Output bits in the stored layout (split: through attn_fwd_bf16_ws)."""
+        if split:
+            launch_ws(self.q, self.k, self.v, self.o, self.layout, mode)
+        else:
+            launch(self.q, self.k, self.v, self.o, self.layout, mode)
         torch.cuda.synchronize()
         return to_bits(self.o)
 
-    def run_logical(self, mode: str) -> np.ndarray:
-        return np.ascontiguousarray(synth.to_logical(self.run(mode), self.layout))
+    def run_logical(self, mode: str, split: bool = False) -> np.ndarray:
+        return np.ascontiguousarray(synth.to_logical(self.run(mode, split), self.layout))
 
 
 def run_raw(q, k, v, layout: str, mode: str) -> np.ndarray:

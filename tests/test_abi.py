@@ -25,7 +25,8 @@ def _enum_values():
 
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
-    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_strerror"]
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_split_plan",
+                     "attn_fwd_bf16_strerror", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
@@ -81,3 +82,72 @@ def test_binding_rejects_missing_library(monkeypatch, tmp_path):
     monkeypatch.setattr(attn, "_LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(ImportError):
         attn.load_library()
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 1, 1, 1, 1, 0, 0, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 0, 1, 1, 1, 0, 0, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, 0, 0, -1), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 5, 0, 0, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, 7, 0, 0), "ATTN_ERR_ROUND"),
+    ((A + 4, B_, C, O_, 1, 1, 1, 1, 0, 0, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, A, 1, 1, 1, 1, 0, 0, 0, 0), "ATTN_ERR_ALIAS"),
+])
+def test_ws_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_ws(*args, 0) == ev[code]
+
+
+def test_workspace_size_argument_errors():
+    import ctypes
+
+    lib = attn.load_library()
+    out = ctypes.c_int64(7)
+    ev = _enum_values()
+    assert lib.attn_fwd_bf16_workspace_size(1, 1, 1, 1, None) == ev["ATTN_ERR_NULL"]
+    assert lib.attn_fwd_bf16_workspace_size(0, 1, 1, 1, ctypes.byref(out)) == ev["ATTN_ERR_SIZE"]
+    assert out.value == 0
+    assert lib.attn_fwd_bf16_workspace_size(1, 1, 1, -5, ctypes.byref(out)) == ev["ATTN_ERR_SIZE"]
+
+
+def _plan(n_work, n_tiles, n_cu=256):
+    return attn.attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu)
+
+
+@pytest.mark.parametrize("n_work,n_tiles,expect", [
+    (816, 513, (768, 48, 5, 103)),    # B=2 H=24 Sq=4097 Sk=32771: 48 items in the last round
+    (2048, 128, (2048, 0, 1, 128)),   # B=4 H=16 Sq=Sk=8192: rounds are full
+    (5120, 512, (5120, 0, 1, 512)),   # B=1 H=40 Sq=Sk=32760
+    (32, 1024, (0, 32, 8, 128)),      # few heads, long keys: 8 ranges each
+    (2, 4, (2, 0, 1, 4)),             # too few tiles to split
+    (4, 47, (0, 4, 10, 5)),           # ranges of >= 4 tiles, none empty
+    (200, 1000, (200, 0, 1, 1000)),   # 200 of 256: splitting by 1 is no split
+])
+def test_split_plan_cases(n_work, n_tiles, expect):
+    assert _plan(n_work, n_tiles) == expect
+
+
+@pytest.mark.parametrize("n_work", [1, 3, 31, 100, 255, 257, 300, 511, 700, 1000, 4097])
+@pytest.mark.parametrize("n_tiles", [1, 4, 7, 8, 63, 513, 2048])
+def test_split_plan_invariants(n_work, n_tiles):
+    n_cu = 256
+    whole, items, splits, tps = _plan(n_work, n_tiles, n_cu)
+    assert whole + items == n_work
+    if items == 0:
+        assert (splits, tps) == (1, n_tiles)
+        return
+    assert whole % n_cu == 0 and 0 < items < n_cu
+    assert splits >= 2 and items * splits <= n_cu          # the last round fits the compute units
+    assert tps >= 4 and (splits - 1) * tps < n_tiles <= splits * tps  # ranges cover the tiles, none empty
+
+
+def test_split_plan_argument_errors():
+    ev = _enum_values()
+    import ctypes
+
+    lib = attn.load_library()
+    out = (ctypes.c_int64 * 4)()
+    assert lib.attn_fwd_bf16_split_plan(1, 1, 1, None) == ev["ATTN_ERR_NULL"]
+    assert lib.attn_fwd_bf16_split_plan(0, 1, 1, out) == ev["ATTN_ERR_SIZE"]
+    assert lib.attn_fwd_bf16_split_plan(1, 0, 1, out) == ev["ATTN_ERR_SIZE"]
+    assert lib.attn_fwd_bf16_split_plan(1, 1, 0, out) == ev["ATTN_ERR_SIZE"]

@@ -13,6 +13,7 @@ import numpy as np
 import pytest
 import torch
 
+import bf16_forward_attention_amd as attn
 import oracle
 from bf16_forward_attention_amd import synth
 from tests.gate import gate
@@ -78,6 +79,14 @@ def _run_config(name):
     # determinism over the whole tensor
     again = dev.run(wl.modes[0])
     assert np.array_equal(again, outs[wl.modes[0]]), "repeated launch changed the output"
+    # the key-range-splitting entry point, where this shape splits
+    if attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
+        for mode in wl.modes:
+            out = dev.run(mode, split=True)
+            res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
+            say(f"  {name} {mode} split: {res.summary()}")
+            assert res.ok, f"{name} {mode} split: {res.summary()}"
+        assert np.array_equal(out, dev.run(wl.modes[-1], split=True)), "split launch not deterministic"
     return wl, inp, outs
 
 
