@@ -17,6 +17,13 @@
 // are per-lane scalars plus one exchange between the two 32-lane halves, and
 // the rescale of the output accumulator is a per-lane multiply.
 //
+// Split key ranges.  One workgroup runs per compute unit at a time, so when
+// the (batch, head, q-tile) items do not fill the last round of compute units
+// the items of that round can run as several workgroups over consecutive key
+// ranges; each leaves unnormalised fp32 rows with their running maximum and
+// sum, and attn_merge_kernel combines them (the same max-shifted sums as the
+// online softmax) before the one rounding to bf16.
+//
 // MFMA 32x32x16 operand layout (lane l, g = l / 32):
 //     A[i][k]: lane supplies row i = l % 32, k = 8g .. 8g+7
 //     B[k][j]: lane supplies column j = l % 32, k = 8g .. 8g+7
@@ -191,8 +198,6 @@ template <int MODE>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp) {
-  // one array per stage, so the compiler can tell the stages apart when it
-  // places waits for the direct-to-LDS loads
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
