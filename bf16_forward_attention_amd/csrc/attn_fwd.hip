@@ -140,7 +140,8 @@ struct Split {
 // the wave).  This goes through ds_bpermute: AMD clang 22 folds
 // fmaxf(r[0], r[1]) of __builtin_amdgcn_permlane32_swap(x, x) into r[0], as
 // if the swap of a register with itself were the identity, which leaves the
-// two halves with different values.
+// two halves with different values (a swap whose second operand is hidden
+// from the compiler is correct but measured no faster here).
 __device__ __forceinline__ float wave_half_max(float x) { return fmaxf(x, __shfl_xor(x, 32)); }
 // fp32 addition is commutative, so both halves get identical bits
 __device__ __forceinline__ float wave_half_sum(float x) { return x + __shfl_xor(x, 32); }
@@ -194,7 +195,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
 }
 
-template <int MODE>
+// SPLIT: the grid may hold split work items (sp describes them); without it
+// every workgroup runs one whole item and the key range is known statically.
+template <int MODE, bool SPLIT>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp) {
@@ -211,7 +214,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   const int n_tiles_all = (Sk + BN - 1) / BN;
   const int id = blockIdx.x;
   int work, t_begin = 0, t_end = n_tiles_all, slot = -1;
-  if (id < sp.n_whole) {
+  if (!SPLIT || id < sp.n_whole) {
     const int xcd = id & 7, local = id >> 3;
     const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
     work = xcd * per + (xcd < rem ? xcd : rem) + local;
@@ -309,14 +312,14 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // free; only rounding depends on it).  Otherwise in the order 0 .. n-1.
   // This workgroup visits positions t_begin .. t_end-1 of that order; loop
   // indices below count from t_begin.
-  const int n_tiles = t_end - t_begin;
+  const int n_tiles = SPLIT ? t_end - t_begin : n_tiles_all;
   const bool ragged = (Sk % BN) != 0;
   // Buffer resources of the K and V rows of the seq-th visited tile.  Past
   // the last tile the range is empty: those loads touch no memory (the
   // hardware range check turns them into zeros), so every iteration issues
   // the same number of loads and the load-count waits need no branches.
   auto tile_rsrc = [&](int t, i32x4& rk, i32x4& rv) __attribute__((always_inline)) {
-    const int seq = t_begin + t;
+    const int seq = SPLIT ? t_begin + t : t;
     const int tile = !ragged ? seq : (seq == 0 ? n_tiles_all - 1 : seq - 1);
     const bool live = t < n_tiles;
     const int base = live ? tile * BN : 0;
@@ -492,7 +495,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 has landed
   __syncthreads();
   qk(S[0], k_st[0]);
-  if (ragged && t_begin == 0) mask_tail(S[0], n_tiles_all - 1);
+  if (ragged && (!SPLIT || t_begin == 0)) mask_tail(S[0], n_tiles_all - 1);
   rowmax(S[0]);
 
   // In the iteration of the last tile the K.Q half reads a stage that holds
@@ -510,7 +513,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 
   // ---- epilogue ----
   const float l_tot = wave_half_sum(l_run);
-  if (slot >= 0) {
+  if (SPLIT && slot >= 0) {
     // partial result of a key range: unnormalised rows, m and l
     const int row = wave * 32 + l32;
     float* prow = sp.part + ((int64_t)slot * BM + row) * D + 4 * grp;
@@ -694,8 +697,12 @@ Geometry make_geometry(int64_t H, int64_t Sq, int64_t Sk, int layout) {
 template <int MODE>
 void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
             int n_qtiles, const Geometry& g, const Split& sp, int64_t n_wg, int n_split_items, hipStream_t s) {
-  hipLaunchKernelGGL(attn_fwd_kernel<MODE>, dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H, Sq, Sk,
-                     n_qtiles, g, sp);
+  if (n_split_items > 0)
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H,
+                       Sq, Sk, n_qtiles, g, sp);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H,
+                       Sq, Sk, n_qtiles, g, sp);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
