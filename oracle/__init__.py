@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for non-causal bf16 forward attention (d = 128).
+"""Plain fp64 CPU oracle for bf16 forward attention (d = 128), unmasked or causal.
 
 TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline
 leg of the benchmark may import this package; the product path never does.
@@ -16,7 +16,13 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
 * ``attn_rows``     -- closed forms (uniform logits, dominant logit, Sk = 1,
                        two-key logistic), midpoint ties, invariants, NaN/Inf
                        rules, mpmath brute force on tiny inputs and a torch
-                       float64 softmax cross-check.
+                       float64 softmax cross-check.  With a causal ``mask``:
+                       the first row of a top-left diagonal returns V_0, a row
+                       equals the unmasked oracle on its visible keys, keys
+                       past the diagonal cannot change it, rows with no
+                       visible key are NaN, mpmath brute force, and torch's
+                       float64 attention with its top-left (``is_causal``) and
+                       bottom-right (``causal_lower_right``) masks.
 * ``softmax_row``   -- rows sum to one; agrees with a library softmax.
 """
 from __future__ import annotations
@@ -33,6 +39,8 @@ _LIB = os.path.join(_HERE, "liboracle.so")
 
 MODES = {"rtne": 0, "rtna": 1, "rtz": 2}
 LAYOUTS = {"bshd": 0, "bhsd": 1}
+# query row i attends to keys j <= i + off: off = 0 ("causal", top left) or Sk - Sq ("causal_br")
+MASKS = {"none": 0, "causal": 1, "causal_br": 2}
 D = 128
 
 _lib = None
@@ -74,6 +82,9 @@ def _load():
         lib.oracle_attn_rows.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int,
                                          i64p, i64, f64p, u16p, ctypes.c_int]
         lib.oracle_attn_rows.restype = ctypes.c_int
+        lib.oracle_attn_rows_masked.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                                i64p, i64, f64p, u16p, ctypes.c_int]
+        lib.oracle_attn_rows_masked.restype = ctypes.c_int
         lib.oracle_softmax_row.argtypes = [u16p, u16p, i64, i64, i64, i64, ctypes.c_int,
                                            i64, i64, i64, f64p]
         lib.oracle_softmax_row.restype = ctypes.c_double
@@ -120,10 +131,12 @@ def _check_inputs(q, k, v, B, H, Sq, Sk, layout):
             raise ValueError(f"{name}: expected contiguous uint16 {shp}, got {t.dtype} {t.shape}")
 
 
-def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nthreads: int | None = None):
+def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nthreads: int | None = None,
+              mask: str = "none"):
     """Exact outputs of the given (b, h, i) query rows and their roundings.
 
-    ``q``/``k``/``v`` are bf16 bit arrays stored in ``layout``.  Returns
+    ``q``/``k``/``v`` are bf16 bit arrays stored in ``layout``; ``mask`` is
+    one of ``MASKS``.  Returns
     ``(o_exact, o_round)``: ``o_exact`` is float64 [n, 128] and ``o_round``
     uint16 [n, 3, 128] in the mode order RTNE, RTNA, RTZ; both follow the
     order of ``rows``.
@@ -141,9 +154,11 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
     srt = np.ascontiguousarray(rows[order])
     o_exact = np.empty((n, D), dtype=np.float64)
     o_round = np.empty((n, 3, D), dtype=np.uint16)
-    rc = _load().oracle_attn_rows(_u16(q), _u16(k), _u16(v), B, H, Sq, Sk, LAYOUTS[layout],
-                                  srt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
-                                  _f64(o_exact), _u16(o_round), nthreads or default_threads())
+    if mask not in MASKS:
+        raise ValueError(f"mask must be one of {sorted(MASKS)}, got {mask!r}")
+    rc = _load().oracle_attn_rows_masked(_u16(q), _u16(k), _u16(v), B, H, Sq, Sk, LAYOUTS[layout], MASKS[mask],
+                                         srt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                         _f64(o_exact), _u16(o_round), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_attn_rows failed with {rc}")
     inv = np.empty_like(order)
@@ -151,7 +166,7 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
     return o_exact[inv], o_round[inv]
 
 
-def attn_all(q, k, v, layout: str, nthreads: int | None = None):
+def attn_all(q, k, v, layout: str, nthreads: int | None = None, mask: str = "none"):
     """Every row: o_exact [B,H,Sq,128] and o_round [3,B,H,Sq,128] (logical order)."""
     if layout == "bshd":
         B, Sq, H, _ = q.shape
@@ -159,7 +174,7 @@ def attn_all(q, k, v, layout: str, nthreads: int | None = None):
         B, H, Sq, _ = q.shape
     bb, hh, ii = np.meshgrid(np.arange(B), np.arange(H), np.arange(Sq), indexing="ij")
     rows = np.stack([bb.ravel(), hh.ravel(), ii.ravel()], axis=1)
-    ex, rd = attn_rows(q, k, v, layout, rows, nthreads)
+    ex, rd = attn_rows(q, k, v, layout, rows, nthreads, mask)
     return ex.reshape(B, H, Sq, D), np.moveaxis(rd.reshape(B, H, Sq, 3, D), 3, 0)
 
 

@@ -1,5 +1,6 @@
 /*
- * attn_oracle.c -- plain fp64 CPU oracle for non-causal bf16 forward attention.
+ * attn_oracle.c -- plain fp64 CPU oracle for bf16 forward attention, without a
+ * mask or with a causal one.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file or the library built from it; only the test-suite, the
@@ -29,6 +30,18 @@
  * NaN and Inf follow from IEEE arithmetic on these steps; nothing is
  * special-cased beyond the propagating maximum of step 3.
  *
+ * Causal mask.  The snilld.dk page lists the causal mask among what the
+ * kernel it describes leaves out and what autoregressive serving needs
+ * (sections "Hvad er udgivet" / What was released and "Autoregressiv serving,
+ * de praktiske hager" / Autoregressive serving, the practical catches); it
+ * gives no definition.  Read here as the usual one: query row i attends only
+ * to the keys j <= i + off, where off = 0 aligns the diagonal at the top left
+ * (row 0 sees key 0) and off = Sk - Sq at the bottom right (the last row sees
+ * every key).  The masked keys do not take part at all: steps 2-5 run over
+ * the visible keys j < n_i = min(max(i + off + 1, 0), Sk) only.  A row with no
+ * visible key has an empty sum, l = 0 and o = 0/0 = NaN, the same result the
+ * formula gives when every logit of a row is -Inf.
+ *
  * Pins (tests/test_oracle_*.py): closed forms, invariants, brute force on
  * tiny inputs, a library softmax cross-check and exhaustive/definitional
  * checks of the rounding and decoding.
@@ -48,6 +61,8 @@
 enum { OR_RTNE = 0, OR_RTNA = 1, OR_RTZ = 2 };
 /* Oracle's own layout codes. BSHD: [B, S, H, D]; BHSD: [B, H, S, D]. */
 enum { OR_BSHD = 0, OR_BHSD = 1 };
+/* Oracle's own mask codes: none, causal aligned top left, causal aligned bottom right. */
+enum { OR_MASK_NONE = 0, OR_MASK_CAUSAL_TOP_LEFT = 1, OR_MASK_CAUSAL_BOTTOM_RIGHT = 2 };
 
 /* ------------------------------------------------------------------------
  * bf16 <-> binary64, from the format definition
@@ -146,10 +161,25 @@ static double max_nan(double a, double b)
     return a > b ? a : b;
 }
 
-/* Steps 2-4 for one query row against a decoded head. On return w[j] holds
- * exp(s_j - m) and the function returns l = sum_j w_j. */
+/* Number of keys query row i attends to (the causal reading in the header). */
+static int64_t visible_keys(int mask, int64_t i, int64_t Sq, int64_t Sk)
+{
+    if (mask == OR_MASK_NONE)
+        return Sk;
+    const int64_t off = mask == OR_MASK_CAUSAL_TOP_LEFT ? 0 : Sk - Sq;
+    int64_t n = i + off + 1;
+    if (n < 0)
+        n = 0;
+    return n < Sk ? n : Sk;
+}
+
+/* Steps 2-4 for one query row against the first Sk keys of a decoded head.
+ * On return w[j] holds exp(s_j - m) and the function returns
+ * l = sum_j w_j (0 when there are no keys). */
 static double row_weights(const double *qrow, const double *Kd, int64_t Sk, double *w)
 {
+    if (Sk == 0)
+        return 0.0;
     const double sqrt_d = sqrt((double)D);
     for (int64_t j = 0; j < Sk; ++j) {
         const double *kr = Kd + j * D;
@@ -190,6 +220,7 @@ typedef struct {
     int layout;
     const double *Kd, *Vd;
     int64_t Sk;
+    int mask;
     const int64_t *rows; /* triples */
     int64_t lo, hi;      /* row range within rows */
     double *o_exact;     /* nrows x D */
@@ -210,9 +241,10 @@ static void *run_job(void *arg)
         int64_t i = jb->rows[3 * r + 2];
         for (int c = 0; c < D; ++c)
             qrow[c] = oracle_bf16_decode(jb->q[offset_of(jb->layout, jb->H, jb->Sq, jb->b, jb->h, i, c)]);
-        double l = row_weights(qrow, jb->Kd, jb->Sk, w);
+        const int64_t n = visible_keys(jb->mask, i, jb->Sq, jb->Sk);
+        double l = row_weights(qrow, jb->Kd, n, w);
         double *o = jb->o_exact + r * D;
-        row_output(w, l, jb->Vd, jb->Sk, o);
+        row_output(w, l, jb->Vd, n, o);
         for (int mode = 0; mode < 3; ++mode)
             for (int c = 0; c < D; ++c)
                 jb->o_round[(r * 3 + mode) * D + c] = oracle_round_bf16(o[c], mode);
@@ -231,23 +263,26 @@ static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int
 }
 
 /*
- * oracle_attn_rows: exact outputs and their three bf16 roundings for a list
- * of query rows.
+ * oracle_attn_rows_masked: exact outputs and their three bf16 roundings for
+ * a list of query rows.
  *   q: [B,Sq,H,128] (BSHD) or [B,H,Sq,128] (BHSD) bf16 bits; k, v likewise with Sk.
+ *   mask: OR_MASK_NONE, OR_MASK_CAUSAL_TOP_LEFT or OR_MASK_CAUSAL_BOTTOM_RIGHT.
  *   rows: nrows triples (b, h, i); rows with equal (b, h) must be adjacent.
  *   o_exact: nrows x 128 binary64;  o_round: nrows x 3 x 128 bf16 bits
  *   (modes in the order RTNE, RTNA, RTZ).
  *   nthreads: worker threads (rows of one head are split among them).
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
-int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                     int64_t B, int64_t H, int64_t Sq, int64_t Sk, int layout,
-                     const int64_t *rows, int64_t nrows,
-                     double *o_exact, uint16_t *o_round, int nthreads)
+int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Sk, int layout, int mask,
+                            const int64_t *rows, int64_t nrows,
+                            double *o_exact, uint16_t *o_round, int nthreads)
 {
     if (!q || !k || !v || !rows || !o_exact || !o_round)
         return -1;
     if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (layout != OR_BSHD && layout != OR_BHSD))
+        return -1;
+    if (mask != OR_MASK_NONE && mask != OR_MASK_CAUSAL_TOP_LEFT && mask != OR_MASK_CAUSAL_BOTTOM_RIGHT)
         return -1;
     if (nthreads < 1)
         nthreads = 1;
@@ -278,7 +313,7 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
         for (int t = 0; t < nt; ++t) {
             job_t *jb = &jobs[t];
             jb->q = q, jb->H = H, jb->Sq = Sq, jb->b = b, jb->h = h, jb->layout = layout;
-            jb->Kd = Kd, jb->Vd = Vd, jb->Sk = Sk, jb->rows = rows;
+            jb->Kd = Kd, jb->Vd = Vd, jb->Sk = Sk, jb->mask = mask, jb->rows = rows;
             jb->lo = r0 + n * t / nt, jb->hi = r0 + n * (t + 1) / nt;
             jb->o_exact = o_exact, jb->o_round = o_round, jb->ok = 0;
         }
@@ -300,6 +335,16 @@ int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
     }
     free(Kd), free(Vd), free(jobs), free(th);
     return status;
+}
+
+/* oracle_attn_rows: the unmasked case of oracle_attn_rows_masked. */
+int oracle_attn_rows(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                     int64_t B, int64_t H, int64_t Sq, int64_t Sk, int layout,
+                     const int64_t *rows, int64_t nrows,
+                     double *o_exact, uint16_t *o_round, int nthreads)
+{
+    return oracle_attn_rows_masked(q, k, v, B, H, Sq, Sk, layout, OR_MASK_NONE, rows, nrows, o_exact, o_round,
+                                   nthreads);
 }
 
 /*

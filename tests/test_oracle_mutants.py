@@ -30,6 +30,11 @@ MUTANTS = {
     "decode_bias": ("mag = ldexp((double)(128 + f), e - 127 - 7);", "mag = ldexp((double)(128 + f), e - 126 - 7);"),
     "no_subnormal_clamp": ("if (e < -126)\n        e = -126;", ""),
     "overflow_rtz_to_inf": ("return mode == OR_RTZ ? (sign | 0x7F7F) : (sign | 0x7F80);", "return sign | 0x7F80;"),
+    "causal_diagonal_excluded": ("int64_t n = i + off + 1;", "int64_t n = i + off;"),
+    "causal_bottom_right_offset_sign": ("OR_MASK_CAUSAL_TOP_LEFT ? 0 : Sk - Sq;", "OR_MASK_CAUSAL_TOP_LEFT ? 0 : Sq - Sk;"),
+    "causal_mask_ignored": ("return n < Sk ? n : Sk;", "return Sk;"),
+    "causal_alignments_swapped": ("OR_MASK_CAUSAL_TOP_LEFT ? 0 : Sk - Sq;", "OR_MASK_CAUSAL_TOP_LEFT ? Sk - Sq : 0;"),
+    "causal_empty_row_zero": ("    if (Sk == 0)\n        return 0.0;", "    if (Sk == 0)\n        return 1.0;"),
 }
 
 
@@ -45,6 +50,7 @@ def test_mutant_is_caught(name, tmp_path):
                     str(mut), "-lm", "-o", str(lib)], check=True)
     env = dict(os.environ, ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
-                        "tests/test_oracle_attention.py", "tests/test_oracle_rounding.py"],
+                        "tests/test_oracle_attention.py", "tests/test_oracle_causal.py",
+                        "tests/test_oracle_rounding.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
