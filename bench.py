@@ -4,10 +4,12 @@
 A step is one call of the library over the whole workload (every query row of
 every head), inputs resident in HBM: attn_fwd_bf16_ws with a preallocated
 workspace when the shape splits its key ranges (then the step is both of its
-kernels), attn_fwd_bf16 otherwise.  Default workload: self-attention
-B=4, H=16, Sq=Sk=8192, d=128, BSHD, RTNE.  Prints one JSON line:
+kernels), attn_fwd_bf16_masked for the causal workloads, attn_fwd_bf16
+otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
+BSHD, RTNE.  Prints one JSON line:
 
-  value      forward TFLOP/s, 4*B*H*Sq*Sk*128 FLOPs / mean step time
+  value      forward TFLOP/s, 4*128 FLOPs per visible (query, key) pair (all
+             B*H*Sq*Sk of them without a mask) / mean step time
   roofline   the kernel against MI355X's dense bf16 MFMA peak, with the
              per-launch duration measured by HIP events on the launch stream
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload's
@@ -75,6 +77,19 @@ def head_rows(wl, n, b, h, stream):
     return [(b, h, i) for i in idx]
 
 
+def visible_keys(wl, rows_i):
+    """Keys each query row attends to: all Sk, or j <= i + off under a causal mask."""
+    i = np.asarray(rows_i, dtype=np.int64)
+    if wl.mask == "none":
+        return np.full(i.shape, wl.Sk, dtype=np.int64)
+    off = 0 if wl.mask == "causal" else wl.Sk - wl.Sq
+    return np.clip(i + off + 1, 0, wl.Sk)
+
+
+def workload_flops(wl) -> float:
+    return 4.0 * 128 * wl.B * wl.H * float(visible_keys(wl, np.arange(wl.Sq)).sum())
+
+
 def cpu_baseline(inp, target_s):
     """Time the oracle, as it stands, on a bounded row sample of this workload.
 
@@ -91,7 +106,7 @@ def cpu_baseline(inp, target_s):
     for n_probe in (2 * threads, 6 * threads):
         probe = head_rows(wl, n_probe, 0, 0, stream=1 << 20)
         t0 = time.perf_counter()
-        oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, probe, threads)
+        oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, probe, threads, mask=wl.mask)
         times.append((len(probe), time.perf_counter() - t0))
     (n1, t1), (n2, t2) = times
     per_row = max((t2 - t1) / max(n2 - n1, 1), 1e-9)
@@ -106,20 +121,31 @@ def cpu_baseline(inp, target_s):
         rows += head_rows(wl, take, bh // wl.H, bh % wl.H, stream=(1 << 21) + bh)
         bh += 1
     t0 = time.perf_counter()
-    oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, threads)
+    oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, threads, mask=wl.mask)
     dt = time.perf_counter() - t0
-    flops = 4.0 * len(rows) * wl.Sk * 128
+    pairs = int(visible_keys(wl, [i for _, _, i in rows]).sum())
+    flops = 4.0 * pairs * 128
+    keys = f"all {wl.Sk} keys each" if wl.mask == "none" else f"{pairs} visible (query, key) pairs"
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} seeded query rows from {bh} heads of {wl.name} (all {wl.Sk} keys each, "
+            "sample": f"{len(rows)} seeded query rows from {bh} heads of {wl.name} ({keys}, "
                       f"fp64 with 3 roundings), {dt:.2f} s"}
 
 
-def kernel_source_sha256() -> str:
+def kernel_code_sha256() -> str:
+    """SHA-256 of the kernel source's code: '//' comments, trailing blanks and
+    empty lines removed (the file has no block comments and no '//' in a
+    string), so that an edit of a comment does not disown the counters."""
     import hashlib
+    import re
 
     path = os.path.join(ROOT, "bf16_forward_attention_amd", "csrc", "attn_fwd.hip")
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()
+    lines = []
+    with open(path) as f:
+        for line in f:
+            code = re.sub(r"//.*$", "", line.rstrip("\n")).rstrip()
+            if code.strip():
+                lines.append(code)
+    return hashlib.sha256("\n".join(lines).encode()).hexdigest()
 
 
 def measured_traffic(workload: str):
@@ -127,8 +153,8 @@ def measured_traffic(workload: str):
 
     The summary (profiles/attn_fwd_traffic_<workload>.txt) records the two
     counters per dispatch, the scale factors a plain copy of known size gave
-    them, and the SHA-256 of the kernel source they were taken on; a summary
-    of another kernel version gives None.
+    them, and the SHA-256 of the kernel code they were taken on
+    (kernel_code_sha256); a summary of another kernel version gives None.
     """
     path = os.path.join(ROOT, "profiles", f"attn_fwd_traffic_{workload}.txt")
     if not os.path.exists(path):
@@ -139,7 +165,7 @@ def measured_traffic(workload: str):
             if "=" in line and not line.lstrip().startswith("#"):
                 k, v = line.split("=", 1)
                 kv[k.strip()] = v.strip()
-    if kv.get("kernel_source_sha256") != kernel_source_sha256():
+    if kv.get("kernel_code_sha256") != kernel_code_sha256():
         return None
     fetch = float(kv["fetch_size_kib_per_launch"]) * float(kv["copy_fetch_scale"])
     write = float(kv["write_size_kib_per_launch"]) * float(kv["copy_write_scale"])
@@ -169,7 +195,8 @@ def main():
     q, k, v = t(inp.q), t(inp.k), t(inp.v)
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
-    ws_bytes = 0 if args.no_split else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
+    masked = wl.mask != "none"
+    ws_bytes = 0 if args.no_split or masked else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
               attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
@@ -178,6 +205,8 @@ def main():
             wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64), torch.cuda.get_device_properties(dev).multi_processor_count)
         entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
                  f"{tps} tiles, {ws_bytes} B workspace")
+    elif masked:
+        entry = f"attn_fwd_bf16_masked({wl.mask})"
     else:
         entry = "attn_fwd_bf16"
     log(f"[bench] entry point: {entry}")
@@ -185,6 +214,8 @@ def main():
     def step():
         if ws_bytes > 0:
             st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+        elif masked:
+            st = attn.attn_fwd_bf16_masked(*args_c, attn.MASKS[wl.mask], stream.cuda_stream)
         else:
             st = attn.attn_fwd_bf16(*args_c, stream.cuda_stream)
         if st != 0:
@@ -208,7 +239,7 @@ def main():
     per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
     total_ms = starts[0].elapsed_time(ends[-1])
     ms_per_step = total_ms / args.steps
-    flops = float(wl.flops)
+    flops = workload_flops(wl)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step (wall {wall_ms / args.steps:.3f}), per-launch mean {per.mean():.3f} "
@@ -230,13 +261,16 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} Sq={wl.Sq} Sk={wl.Sk} d=128 {wl.layout.upper()} "
-                               f"{mode.upper()}", "B": wl.B, "H": wl.H, "Sq": wl.Sq, "Sk": wl.Sk,
-                   "head_dim": 128, "layout": wl.layout, "round_mode": mode},
+                               f"{mode.upper()}" + (f" {wl.mask}" if masked else ""),
+                   "B": wl.B, "H": wl.H, "Sq": wl.Sq, "Sk": wl.Sk,
+                   "head_dim": 128, "layout": wl.layout, "round_mode": mode, "mask": wl.mask,
+                   "flops_per_step": flops},
         "entry_point": entry,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
                      "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                      "traffic": measured_traffic(wl.name),
-                     "kernel": f"attn_fwd_kernel<{mode.upper()}>" + (" + attn_merge_kernel" if ws_bytes else ""),
+                     "kernel": f"attn_fwd_kernel<{mode.upper()}{', causal' if masked else ''}>"
+                               + (" + attn_merge_kernel" if ws_bytes else ""),
                      "launch_ms_mean": round(float(per.mean()), 4),
                      "launch_ms_median": round(float(np.median(per)), 4)},
     }
@@ -247,7 +281,7 @@ def main():
         log("[bench] cpu baseline (oracle)")
         result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
         rows = sample_rows(wl, args.parity_rows, stream=(1 << 20) + 2)
-        ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows)
+        ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask=wl.mask)
         logical = synth.to_logical(out_bits, wl.layout)
         got = np.stack([logical[b, h, i] for b, h, i in rows])
         res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)

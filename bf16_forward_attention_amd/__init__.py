@@ -5,10 +5,11 @@ only, every step of the computation runs in the HIP library
 ``libattn_fwd.so``.  PyTorch is used for device memory and streams.
 
     attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
+    attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream) -> status
     attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
     attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
-    attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True) -> torch.Tensor
+    attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True, mask="none") -> torch.Tensor
 """
 from __future__ import annotations
 
@@ -16,9 +17,9 @@ import ctypes
 import os
 
 __all__ = [
-    "attn_fwd_bf16", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_split_plan",
-    "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
-    "AttnError", "LAYOUTS", "ROUND_MODES", "library_path", "load_library",
+    "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size",
+    "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
+    "AttnError", "LAYOUTS", "ROUND_MODES", "MASKS", "library_path", "load_library",
 ]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -27,6 +28,8 @@ _LIB_PATH = os.path.join(_HERE, "libattn_fwd.so")
 # values of attn_layout_t / attn_round_t in include/attn_fwd.h
 LAYOUTS = {"bshd": 0, "bhsd": 1}
 ROUND_MODES = {"rtne": 0, "rtna": 1, "rtz": 2}
+# values of attn_mask_t: query row i attends to keys j <= i + off, off = 0 or Sk - Sq
+MASKS = {"none": 0, "causal": 1, "causal_br": 2}
 HEAD_DIM = 128
 
 _lib = None
@@ -54,6 +57,9 @@ def load_library():
         vp, i64 = ctypes.c_void_p, ctypes.c_int64
         lib.attn_fwd_bf16.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
         lib.attn_fwd_bf16.restype = ctypes.c_int
+        lib.attn_fwd_bf16_masked.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, vp]
+        lib.attn_fwd_bf16_masked.restype = ctypes.c_int
         lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
                                          vp]
         lib.attn_fwd_bf16_ws.restype = ctypes.c_int
@@ -73,6 +79,12 @@ def attn_fwd_bf16(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: i
                   layout: int, round_mode: int, stream: int) -> int:
     """The C entry point with raw device addresses; returns the status code."""
     return load_library().attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream)
+
+
+def attn_fwd_bf16_masked(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int,
+                         layout: int, round_mode: int, mask: int, stream: int) -> int:
+    """The masked C entry point with raw device addresses; returns the status code."""
+    return load_library().attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream)
 
 
 def attn_fwd_bf16_ws(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int, layout: int,
@@ -123,19 +135,23 @@ def _dims(q, k, layout: str):
 
 
 def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None,
-             split: bool = True):
+             split: bool = True, mask: str = "none"):
     """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
 
     ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H,128] for "bshd", or
     [B,H,S,128] for "bhsd"; all contiguous bf16 on one device.  Enqueued on
     ``stream`` (default: torch's current stream on that device).  With
     ``split`` the key range may be split (attn_fwd_bf16_ws, workspace from
-    torch); without, the single-pass attn_fwd_bf16.
+    torch); without, the single-pass attn_fwd_bf16.  ``mask`` "causal" or
+    "causal_br" (attn_fwd_bf16_masked) lets row i see keys j <= i or
+    j <= i + Sk - Sq only; masked calls run single-pass.
     """
     import torch
 
     if round_mode not in ROUND_MODES:
         raise ValueError(f"round_mode must be one of {sorted(ROUND_MODES)}, got {round_mode!r}")
+    if mask not in MASKS:
+        raise ValueError(f"mask must be one of {sorted(MASKS)}, got {mask!r}")
     B, H, Sq, Sk = _dims(q, k, layout)
     if tuple(v.shape) != tuple(k.shape):
         raise ValueError("v must have the shape of k")
@@ -151,8 +167,11 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split else 0
-        if ws_bytes > 0:
+        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and mask == "none" else 0
+        if mask != "none":
+            status = attn_fwd_bf16_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
+                                          LAYOUTS[layout], ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
+        elif ws_bytes > 0:
             ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
             status = attn_fwd_bf16_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
                                       LAYOUTS[layout], ROUND_MODES[round_mode], ws.data_ptr(), ws_bytes,

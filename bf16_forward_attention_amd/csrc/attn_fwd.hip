@@ -1,4 +1,5 @@
-// attn_fwd.hip -- fused non-causal bf16 forward attention for MI355X (gfx950).
+// attn_fwd.hip -- fused bf16 forward attention for MI355X (gfx950), without a
+// mask or with a causal one.
 //
 // O = softmax(Q K^T / sqrt(128)) V per (batch, head, query row), the
 // operation the snilld.dk page "Open source attention kernel in HIP beats
@@ -197,10 +198,16 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // SPLIT: the grid may hold split work items (sp describes them); without it
 // every workgroup runs one whole item and the key range is known statically.
-template <int MODE, bool SPLIT>
+// CAUSAL (not with SPLIT): query row r attends to the keys
+// j <= min(r + causal_off, Sk - 1) only.  The workgroup visits the key tiles
+// 0 .. up to its last row's limit in order (so the q-tiles of a head stream
+// the same tiles together, as without a mask): those every row sees whole in
+// a loop without mask code, then the diagonal ones (some row's limit falls
+// inside or before them) with the mask applied beside the row maxima.
+template <int MODE, bool SPLIT, bool CAUSAL>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp) {
+    uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp, int causal_off) {
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
@@ -224,7 +231,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     t_begin = (slot % sp.splits) * sp.tiles_per_split;
     t_end = t_begin + sp.tiles_per_split < n_tiles_all ? t_begin + sp.tiles_per_split : n_tiles_all;
   }
-  const int qt = work % n_qtiles;
+  // causal: a head's q-tiles in decreasing order, the ones with the most
+  // visible keys dispatched first
+  const int qt = CAUSAL ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles;
   const int bh = work / n_qtiles;
   const int h = bh % H, b = bh / H;
 
@@ -312,15 +321,33 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // free; only rounding depends on it).  Otherwise in the order 0 .. n-1.
   // This workgroup visits positions t_begin .. t_end-1 of that order; loop
   // indices below count from t_begin.
-  const int n_tiles = SPLIT ? t_end - t_begin : n_tiles_all;
+  int n_tiles = SPLIT ? t_end - t_begin : n_tiles_all;
   const bool ragged = (Sk % BN) != 0;
+  // CAUSAL: this lane's last visible key (negative: none); the number of key
+  // tiles the workgroup visits, up to its last row's limit (at least one:
+  // when no row sees a key, tile 0 is visited fully masked, l stays 0 and
+  // every row ends as 0 * (1/0) = NaN); the first diagonal tile diag0 (the
+  // first row's limit falls inside it: every earlier tile is visible to all
+  // rows).
+  int row_lim = 0, diag0 = 0;
+  if constexpr (CAUSAL) {
+    const int64_t last_key = (int64_t)Sk - 1;
+    const int64_t lim = (int64_t)qrow + causal_off;
+    row_lim = (int)(lim < last_key ? lim : last_key);
+    const int64_t r_last = ((int64_t)qt * BM + BM < Sq ? (int64_t)qt * BM + BM : (int64_t)Sq) - 1;
+    const int64_t hi = r_last + causal_off < last_key ? r_last + causal_off : last_key;
+    n_tiles = hi < 0 ? 1 : (int)(hi / BN) + 1;
+    const int64_t r0 = (int64_t)qt * BM + causal_off;
+    const int64_t lo = r0 < last_key ? r0 : last_key;
+    diag0 = lo < 0 ? 0 : (int)((lo + 1) / BN);
+  }
   // Buffer resources of the K and V rows of the seq-th visited tile.  Past
   // the last tile the range is empty: those loads touch no memory (the
   // hardware range check turns them into zeros), so every iteration issues
   // the same number of loads and the load-count waits need no branches.
   auto tile_rsrc = [&](int t, i32x4& rk, i32x4& rv) __attribute__((always_inline)) {
     const int seq = SPLIT ? t_begin + t : t;
-    const int tile = !ragged ? seq : (seq == 0 ? n_tiles_all - 1 : seq - 1);
+    const int tile = CAUSAL || !ragged ? seq : (seq == 0 ? n_tiles_all - 1 : seq - 1);
     const bool live = t < n_tiles;
     const int base = live ? tile * BN : 0;
     const int valid = Sk - base < BN ? Sk - base : BN;
@@ -328,20 +355,25 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     rk = make_rsrc(Kh + (int64_t)base * g.k_row, nrec);
     rv = make_rsrc(Vh + (int64_t)base * g.k_row, nrec);
   };
-  // this wave's two 1 KiB pieces of a K (or V) tile, straight into LDS
-  auto dma_k = [&](const i32x4& rk, uint8_t* kdst, int u) __attribute__((always_inline)) {
-    lds_dma_b128(rk, __builtin_amdgcn_readfirstlane(lds_addr(kdst + 1024 * (2 * wave + u))), k_src[u]);
+  // this wave's two 1 KiB pieces of a K (or V) tile of LDS stage `stage`,
+  // straight into LDS.  `lw` is the wave's LDS base (its pieces start 2 KiB
+  // apart); the loop passes it through an empty asm each iteration so that the
+  // compiler adds the stage offsets where they are used instead of keeping
+  // sixteen precomputed addresses in scalar registers across the loop.
+  const uint32_t lds_wave = __builtin_amdgcn_readfirstlane(lds_addr(lds) + 2048u * (uint32_t)wave);
+  auto dma_k = [&](const i32x4& rk, uint32_t lw, int stage, int u) __attribute__((always_inline)) {
+    lds_dma_b128(rk, lw + (uint32_t)(stage * TILE_BYTES + 1024 * u), k_src[u]);
   };
-  auto dma_v = [&](const i32x4& rv, uint8_t* vdst, int u) __attribute__((always_inline)) {
-    lds_dma_b128(rv, __builtin_amdgcn_readfirstlane(lds_addr(vdst + 1024 * (2 * wave + u))), v_src[u]);
+  auto dma_v = [&](const i32x4& rv, uint32_t lw, int stage, int u) __attribute__((always_inline)) {
+    lds_dma_b128(rv, lw + (uint32_t)((NSTAGE + stage) * TILE_BYTES + 1024 * u), v_src[u]);
   };
-  auto issue_loads = [&](int seq, uint8_t* kdst, uint8_t* vdst) __attribute__((always_inline)) {
+  auto issue_loads = [&](int seq, int stage) __attribute__((always_inline)) {
     i32x4 rk, rv;
     tile_rsrc(seq, rk, rv);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
-      dma_k(rk, kdst, u);
-      dma_v(rv, vdst, u);
+      dma_k(rk, lds_wave, stage, u);
+      dma_v(rv, lds_wave, stage, u);
     }
   };
 
@@ -375,6 +407,16 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 #pragma unroll
       for (int n = 0; n < 16; ++n)
         if (base + 32 * kb + 16 * grp + n >= Sk) s[kb][n] = -__builtin_inff();
+  };
+  // CAUSAL: keys past this lane's limit in key tile `tile` get a -Inf logit
+  // (element n of block kb holds key 64 tile + 32kb + 16grp + n)
+  auto mask_causal = [&](f32x16 (&s)[2], int tile) __attribute__((always_inline)) {
+    const int rel = row_lim - tile * BN - 16 * grp;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int n = 0; n < 16; ++n)
+        if (32 * kb + n > rel) s[kb][n] = -__builtin_inff();
   };
   auto rowmax = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
     float m = s[0][0];
@@ -433,7 +475,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   };
   // Region B: P.V of the current tile (V stage vt) interleaved with the row
   // maxima of the next tile's logits: one MFMA, then two maxima.
-  auto pv_rowmax = [&](int vstage, const f32x16 (&sn)[2], auto&& hook) __attribute__((always_inline)) {
+  // MASKED: the logits of key tile `ntile` get the causal mask first (keys
+  // past the lane's limit become -Inf), two per MFMA like the maxima
+  auto pv_rowmax = [&](auto masked_c, int vstage, f32x16 (&sn)[2], int ntile, auto&& hook)
+                       __attribute__((always_inline)) {
+    constexpr bool MASKED = decltype(masked_c)::value;
+    const int rel = row_lim - ntile * BN - 16 * grp;
     bf16x8 va[16];
     auto vread = [&](int i) __attribute__((always_inline)) {
       const int kb = i >> 3, hh = (i >> 2) & 1, db = i & 3;
@@ -452,6 +499,11 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf[kb][hh], acc[db], 0, 0, 0);
       if (i == kHookAt0) hook(0);
       if (i == kHookAt1) hook(1);
+      if (MASKED) {
+        const int n = 2 * (i & 7), key = 32 * (i >> 3) + n;
+        if (key > rel) sn[i >> 3][n] = -__builtin_inff();
+        if (key + 1 > rel) sn[i >> 3][n + 1] = -__builtin_inff();
+      }
       m = fmaxf(m, sn[i >> 3][2 * (i & 7)]);
       m = fmaxf(m, sn[i >> 3][2 * (i & 7) + 1]);
     }
@@ -468,7 +520,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // t+2 may remain in flight); the barrier makes every wave's loads visible
   // and frees stage (t+3) % 4, last read in iteration t-1, for the loads of
   // tile t+3.
-  auto body = [&](auto st_c, int t) __attribute__((always_inline)) {
+  auto body = [&](auto st_c, auto masked_c, int t) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value, P = ST & 1;
     rescale();
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only the loads of tile t+2 may still be in flight
@@ -477,11 +529,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     // stalls this wave while its matrix work is under way
     i32x4 rk, rv;
     tile_rsrc(t + 3, rk, rv);
+    uint32_t lw = lds_wave;
+    asm volatile("" : "+s"(lw));
     qk_weights(S[1 - P], S[P], k_st[(ST + 1) % NSTAGE],
-               [&](int u) __attribute__((always_inline)) { dma_k(rk, k_st[(ST + 3) % NSTAGE], u); });
-    pv_rowmax(ST, S[1 - P],
-              [&](int u) __attribute__((always_inline)) { dma_v(rv, v_st[(ST + 3) % NSTAGE], u); });
+               [&](int u) __attribute__((always_inline)) { dma_k(rk, lw, (ST + 3) % NSTAGE, u); });
+    pv_rowmax(masked_c, ST, S[1 - P], t + 1,
+              [&](int u) __attribute__((always_inline)) { dma_v(rv, lw, (ST + 3) % NSTAGE, u); });
   };
+  using Plain = std::false_type;
+  using Masked = std::true_type;
   using S0 = std::integral_constant<int, 0>;
   using S1 = std::integral_constant<int, 1>;
   using S2 = std::integral_constant<int, 2>;
@@ -489,26 +545,58 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 
   // prologue: tiles 0..2 of the visiting order in flight, logits and row
   // maxima of the first (masked when it is the ragged one)
-  issue_loads(0, k_st[0], v_st[0]);
-  issue_loads(1, k_st[1], v_st[1]);
-  issue_loads(2, k_st[2], v_st[2]);
+  issue_loads(0, 0);
+  issue_loads(1, 1);
+  issue_loads(2, 2);
   __builtin_amdgcn_s_waitcnt(0x0F78);  // vmcnt(8): tile 0 has landed
   __syncthreads();
   qk(S[0], k_st[0]);
-  if (ragged && (!SPLIT || t_begin == 0)) mask_tail(S[0], n_tiles_all - 1);
+  if (CAUSAL) {
+    if (diag0 == 0) mask_causal(S[0], 0);
+  } else if (ragged && (!SPLIT || t_begin == 0)) {
+    mask_tail(S[0], n_tiles_all - 1);
+  }
   rowmax(S[0]);
 
   // In the iteration of the last tile the K.Q half reads a stage that holds
   // no new tile; its logits are never used.
-  for (int t = 0;;) {
-    body(S0{}, t);
-    if (++t == n_tiles) break;
-    body(S1{}, t);
-    if (++t == n_tiles) break;
-    body(S2{}, t);
-    if (++t == n_tiles) break;
-    body(S3{}, t);
-    if (++t == n_tiles) break;
+  if constexpr (CAUSAL) {
+    // Iteration t masks the logits of tile t+1.  The first n_plain
+    // iterations (whole rounds of the four stages, their next tiles all
+    // before diag0) need no mask; the rest mask whatever tile comes next (a
+    // mask on a tile every row sees whole changes nothing).
+    const int n_plain = diag0 > 0 ? ((diag0 - 1) & ~3) : 0;
+    int t = 0;
+    while (t < n_plain) {
+      body(S0{}, Plain{}, t);
+      body(S1{}, Plain{}, t + 1);
+      body(S2{}, Plain{}, t + 2);
+      body(S3{}, Plain{}, t + 3);
+      t += 4;
+    }
+    while (t < n_tiles) {
+      body(S0{}, Masked{}, t);
+      if (++t == n_tiles) break;
+      body(S1{}, Masked{}, t);
+      if (++t == n_tiles) break;
+      body(S2{}, Masked{}, t);
+      if (++t == n_tiles) break;
+      body(S3{}, Masked{}, t);
+      ++t;
+    }
+  } else {
+    // (written as an exit test after each body: a test before the first one
+    // makes this compiler spill the pipeline's registers)
+    for (int t = 0;;) {
+      body(S0{}, Plain{}, t);
+      if (++t == n_tiles) break;
+      body(S1{}, Plain{}, t);
+      if (++t == n_tiles) break;
+      body(S2{}, Plain{}, t);
+      if (++t == n_tiles) break;
+      body(S3{}, Plain{}, t);
+      if (++t == n_tiles) break;
+    }
   }
 
   // ---- epilogue ----
@@ -696,13 +784,18 @@ Geometry make_geometry(int64_t H, int64_t Sq, int64_t Sk, int layout) {
 
 template <int MODE>
 void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
-            int n_qtiles, const Geometry& g, const Split& sp, int64_t n_wg, int n_split_items, hipStream_t s) {
+            int n_qtiles, const Geometry& g, const Split& sp, int64_t n_wg, int n_split_items, int mask,
+            hipStream_t s) {
+  const int causal_off = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
   if (n_split_items > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H,
-                       Sq, Sk, n_qtiles, g, sp);
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
+                       o, H, Sq, Sk, n_qtiles, g, sp, 0);
+  else if (mask != ATTN_MASK_NONE)
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
+                       o, H, Sq, Sk, n_qtiles, g, sp, causal_off);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v, o, H,
-                       Sq, Sk, n_qtiles, g, sp);
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
+                       o, H, Sq, Sk, n_qtiles, g, sp, 0);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
@@ -711,7 +804,7 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
 }
 
 int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t Sq, int64_t Sk, int layout,
-        int round_mode, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
+        int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
   const Geometry g = make_geometry(H, Sq, Sk, layout);
   Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
   if (plan.n_split_items > 0) {
@@ -725,13 +818,16 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
   const int nsi = (int)plan.n_split_items;
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
-      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
+      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
+                             s);
       break;
     case ATTN_ROUND_RTNA:
-      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
+      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
+                             s);
       break;
     default:
-      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, s);
+      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
+                             s);
       break;
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -748,7 +844,21 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, pb, whole, nullptr, stream);
+  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream);
+}
+
+extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                                    int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* stream) {
+  Problem pb;
+  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  if (st != ATTN_OK) return st;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
+  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream);
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {
@@ -797,7 +907,7 @@ extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, voi
         overlaps(workspace, need, v, pb.bytes_k) || overlaps(workspace, need, o, pb.bytes_q))
       return ATTN_ERR_ALIAS;
   }
-  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, pb, plan, workspace, stream);
+  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, plan, workspace, stream);
 }
 
 extern "C" const char* attn_fwd_bf16_strerror(int status) {
@@ -812,6 +922,7 @@ extern "C" const char* attn_fwd_bf16_strerror(int status) {
     case ATTN_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X) or cannot be queried";
     case ATTN_ERR_HIP: return "the HIP kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_bf16_workspace_size reports";
+    case ATTN_ERR_MASK: return "mask is not an attn_mask_t value";
     default: return "unknown status";
   }
 }

@@ -225,9 +225,11 @@ class Workload:
     inject_k_specials: bool = False  # one NaN, one +Inf, one -Inf in K
     checked_rows_per_head: int = 0  # 0: every row is checkable
     seed: int = 0
+    mask: str = "none"  # key mask the workload is run with: "none", "causal", "causal_br"
 
     @property
     def flops(self) -> int:
+        """4 d FLOP per (query, key) pair of the unmasked problem."""
         return 4 * self.B * self.H * self.Sq * self.Sk * D
 
 
@@ -240,6 +242,10 @@ WORKLOADS = {
         "dit_stress", 1, 40, 32760, 32760, "bshd", ("rtna",),
         qk_sigma=2.0, v_dist="uniform", scaled_row_fraction=0.001, inject_k_specials=True,
     ),
+    # causal self-attention at the benchmark shape, and a chunk of new queries
+    # against a longer key cache (diagonal at the bottom right, ragged tiles)
+    "self8k_causal": Workload("self8k_causal", 4, 16, 8192, 8192, "bshd", ("rtne",), mask="causal"),
+    "prefill_br": Workload("prefill_br", 2, 24, 4097, 32771, "bshd", ("rtz",), mask="causal_br"),
 }
 
 
@@ -325,8 +331,8 @@ def generate(wl: Workload) -> Inputs:
 
 
 def small(B: int, H: int, Sq: int, Sk: int, layout: str = "bshd", seed: int = 0,
-          qk_sigma: float = 1.0, v_dist: str = "normal") -> Inputs:
+          qk_sigma: float = 1.0, v_dist: str = "normal", mask: str = "none") -> Inputs:
     """A small i.i.d. workload for parity tests."""
-    wl = Workload(f"small_{B}x{H}x{Sq}x{Sk}_{layout}", B, H, Sq, Sk, layout, MODES,
-                  qk_sigma=qk_sigma, v_dist=v_dist, seed=seed)
+    wl = Workload(f"small_{B}x{H}x{Sq}x{Sk}_{layout}_{mask}", B, H, Sq, Sk, layout, MODES,
+                  qk_sigma=qk_sigma, v_dist=v_dist, seed=seed, mask=mask)
     return generate(wl)

@@ -7,7 +7,8 @@
  *
  *     O[b,h,i,:] = softmax_j( Q[b,h,i,:] . K[b,h,j,:] / sqrt(128) ) V[b,h,j,:]
  *
- * non-causal, head_dim fixed at 128, one head count shared by Q, K and V, any
+ * without a mask (attn_fwd_bf16_masked adds a causal one), head_dim fixed at
+ * 128, one head count shared by Q, K and V, any
  * query length Sq and key length Sk (cross-attention allowed), inputs read in
  * the BSHD or BHSD layout without a transpose (same page, section "Hvad er
  * udgivet" / What was released).  Output is bf16, rounded per call in one of
@@ -43,7 +44,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 2
+#define ATTN_FWD_ABI_VERSION 3
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -57,6 +58,13 @@ typedef enum {
     ATTN_ROUND_RTZ = 2   /* toward zero */
 } attn_round_t;
 
+/* Key mask of attn_fwd_bf16_masked: query row i attends to keys j <= i + off. */
+typedef enum {
+    ATTN_MASK_NONE = 0,               /* every key */
+    ATTN_MASK_CAUSAL = 1,             /* off = 0: diagonal at the top left */
+    ATTN_MASK_CAUSAL_BOTTOM_RIGHT = 2 /* off = Sk - Sq: diagonal at the bottom right */
+} attn_mask_t;
+
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,   /* a tensor pointer is NULL */
@@ -67,7 +75,8 @@ typedef enum {
     ATTN_ERR_ALIAS = 6,  /* o overlaps q, k or v */
     ATTN_ERR_DEVICE = 7, /* the current device is not gfx950, or cannot be queried */
     ATTN_ERR_HIP = 8,    /* the kernel launch failed */
-    ATTN_ERR_WORKSPACE = 9 /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
+    ATTN_ERR_WORKSPACE = 9, /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
+    ATTN_ERR_MASK = 10      /* mask is not an attn_mask_t value */
 } attn_status_t;
 
 /*
@@ -124,6 +133,33 @@ int attn_fwd_bf16_ws(const void *q, const void *k, const void *v, void *o,
                      int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                      int layout, int round_mode, void *workspace,
                      int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_bf16_masked -- attn_fwd_bf16 with a key mask.
+ *
+ * The snilld.dk page names the causal mask among what the kernel it describes
+ * lacks and what autoregressive serving needs (sections "Hvad er udgivet" /
+ * What was released and "Autoregressiv serving, de praktiske hager") without
+ * defining it; this is the usual definition.  With ATTN_MASK_CAUSAL query row
+ * i attends to the keys j <= i (row 0 sees key 0); with
+ * ATTN_MASK_CAUSAL_BOTTOM_RIGHT to the keys j <= i + Sk - Sq (the last row
+ * sees every key, as when Sq new queries follow Sk - Sq cached keys).  Masked
+ * keys take no part in the row's softmax.  A row with no visible key (only
+ * possible at the bottom right with Sq > Sk: rows i < Sq - Sk) is NaN, the
+ * 0/0 of an empty softmax, as for a row whose logits are all -Inf.  A NaN or
+ * Inf in V at a masked key is outside the contract (the matrix core
+ * multiplies it by a zero weight).  ATTN_MASK_NONE is exactly attn_fwd_bf16.
+ *
+ *   mask            : attn_mask_t.
+ *   other arguments : as attn_fwd_bf16.
+ *
+ * Status codes as attn_fwd_bf16, plus ATTN_ERR_MASK.  The work of a causal
+ * call is the visible (query, key) pairs only: about half of the unmasked
+ * call's for Sq = Sk.
+ */
+int attn_fwd_bf16_masked(const void *q, const void *k, const void *v, void *o,
+                         int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                         int layout, int round_mode, int mask, void *stream);
 
 /*
  * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs

@@ -86,3 +86,25 @@ def tie_inputs(vals):
     k = np.zeros((1, 1, n, D), np.uint16)
     v = np.repeat(np.asarray(vals, np.uint16)[:, None], D, axis=1).reshape(1, 1, n, D)
     return q, k, v
+
+
+def diagonal_dominant(B, H, Sq, Sk, off, seed=0):
+    """Inputs where row i's key j = i + off (when 0 <= j < Sk) dominates.
+
+    Needs Sq <= 127: row i points along direction c_i = 1 + i; column c_i of K
+    is 0 except k[i + off, c_i] = 128, so that key's logit is ~1448 and every
+    other key's is 0 or a random multiple of 128 * k / sqrt(128) far below it
+    (K's other columns stay random).  A row whose key lies past the end of K
+    has q = 0.  Returns (q, k, v).
+    """
+    assert Sq <= D - 1
+    q = np.zeros((B, H, Sq, D), np.uint16)
+    k = randn_bits((B, H, Sk, D), seed + 1)
+    v = randn_bits((B, H, Sk, D), seed + 2)
+    k[:, :, :, 1:Sq + 1] = 0
+    for i in range(Sq):
+        j = i + off
+        if 0 <= j < Sk:
+            q[:, :, i, 1 + i] = bf(128.0)
+            k[:, :, j, 1 + i] = bf(128.0)
+    return q, k, v

@@ -42,6 +42,22 @@ def launch(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, l
         raise attn.AttnError(st)
 
 
+def launch_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
+                  mask: str, stream: torch.cuda.Stream | None = None) -> None:
+    """Call attn_fwd_bf16_masked through the C ABI with raw device pointers."""
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Sk = k.shape[1]
+    else:
+        B, H, Sq, _ = q.shape
+        Sk = k.shape[2]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = attn.attn_fwd_bf16_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, Sq, Sk,
+                                   attn.LAYOUTS[layout], attn.ROUND_MODES[mode], attn.MASKS[mask], s.cuda_stream)
+    if st != 0:
+        raise attn.AttnError(st)
+
+
 def launch_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
               stream: torch.cuda.Stream | None = None) -> int:
     """Call attn_fwd_bf16_ws (key ranges split when it pays) with a torch-allocated
@@ -72,29 +88,37 @@ class Dev:
         self.q, self.k, self.v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
         self.o = torch.empty_like(self.q)
 
-    def run(self, mode: str, split: bool = False) -> np.ndarray:
-        """Output bits in the stored layout (split: through attn_fwd_bf16_ws)."""
-        if split:
+    def run(self, mode: str, split: bool = False, mask: str | None = None) -> np.ndarray:
+        """Output bits in the stored layout (split: through attn_fwd_bf16_ws; a
+        mask, or the workload's own, through attn_fwd_bf16_masked)."""
+        mask = self.inp.wl.mask if mask is None else mask
+        if mask != "none":
+            launch_masked(self.q, self.k, self.v, self.o, self.layout, mode, mask)
+        elif split:
             launch_ws(self.q, self.k, self.v, self.o, self.layout, mode)
         else:
             launch(self.q, self.k, self.v, self.o, self.layout, mode)
         torch.cuda.synchronize()
         return to_bits(self.o)
 
-    def run_logical(self, mode: str, split: bool = False) -> np.ndarray:
-        return np.ascontiguousarray(synth.to_logical(self.run(mode, split), self.layout))
+    def run_logical(self, mode: str, split: bool = False, mask: str | None = None) -> np.ndarray:
+        return np.ascontiguousarray(synth.to_logical(self.run(mode, split, mask), self.layout))
 
 
-def run_raw(q, k, v, layout: str, mode: str) -> np.ndarray:
+def run_raw(q, k, v, layout: str, mode: str, mask: str = "none") -> np.ndarray:
     """Stored-layout bits in, stored-layout bits out."""
     dq, dk, dv = to_device(q), to_device(k), to_device(v)
     o = torch.empty_like(dq)
-    launch(dq, dk, dv, o, layout, mode)
+    if mask == "none":
+        launch(dq, dk, dv, o, layout, mode)
+    else:
+        launch_masked(dq, dk, dv, o, layout, mode, mask)
     torch.cuda.synchronize()
     return to_bits(o)
 
 
-def run_logical(q, k, v, layout: str, mode: str) -> np.ndarray:
+def run_logical(q, k, v, layout: str, mode: str, mask: str = "none") -> np.ndarray:
     """Logical [B,H,S,128] bits in and out, stored in ``layout`` on the way."""
-    out = run_raw(synth.to_layout(q, layout), synth.to_layout(k, layout), synth.to_layout(v, layout), layout, mode)
+    out = run_raw(synth.to_layout(q, layout), synth.to_layout(k, layout), synth.to_layout(v, layout), layout, mode,
+                  mask)
     return np.ascontiguousarray(synth.to_logical(out, layout))

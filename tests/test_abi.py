@@ -25,7 +25,7 @@ def _enum_values():
 
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
-    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_split_plan",
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_masked", "attn_fwd_bf16_split_plan",
                      "attn_fwd_bf16_strerror", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
@@ -43,6 +43,8 @@ def test_enum_values_match_binding():
     assert ev["ATTN_ROUND_RTNE"] == attn.ROUND_MODES["rtne"]
     assert ev["ATTN_ROUND_RTNA"] == attn.ROUND_MODES["rtna"]
     assert ev["ATTN_ROUND_RTZ"] == attn.ROUND_MODES["rtz"]
+    assert ev["ATTN_MASK_NONE"] == attn.MASKS["none"] and ev["ATTN_MASK_CAUSAL"] == attn.MASKS["causal"]
+    assert ev["ATTN_MASK_CAUSAL_BOTTOM_RIGHT"] == attn.MASKS["causal_br"]
 
 
 def test_abi_version_and_strerror():
@@ -75,6 +77,29 @@ A, B_, C, O_ = 0x10000, 0x20000, 0x30000, 0x40000  # distinct aligned fake addre
 def test_argument_errors_before_any_hip_call(args, code):
     ev = _enum_values()
     assert attn.attn_fwd_bf16(*args, 0) == ev[code]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 1, 1, 1, 1, 0, 0, 1), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 1, 1, 0, 1, 0, 0, 1), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 4, 0, 1), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, -1, 2), "ATTN_ERR_ROUND"),
+    ((A, B_ + 8, C, O_, 1, 1, 1, 1, 0, 0, 1), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, C, 1, 1, 1, 1, 0, 0, 2), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, 0, 3), "ATTN_ERR_MASK"),
+    ((A, B_, C, O_, 1, 1, 1, 1, 0, 0, -1), "ATTN_ERR_MASK"),
+])
+def test_masked_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_masked(*args, 0) == ev[code]
+
+
+def test_binding_rejects_unknown_mask_name():
+    import torch
+
+    q = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        attn.attn_fwd(q, q, q, mask="upper")
 
 
 def test_binding_rejects_missing_library(monkeypatch, tmp_path):

@@ -40,7 +40,7 @@ def _rows_for(wl, n_random=512):
         total = wl.B * wl.H * wl.Sq
         flat = synth.floyd_sample(wl.seed, synth.TID_SUBSET, total, min(n_random, total), stream=999)
         rows = {(f // (wl.H * wl.Sq), (f // wl.Sq) % wl.H, f % wl.Sq) for f in flat}
-    edge = [0, 1, 127, 128, 255, 256, wl.Sq - 2, wl.Sq - 1]
+    edge = [0, 1, 63, 64, 127, 128, 255, 256, 257, wl.Sq - 257, wl.Sq - 256, wl.Sq - 2, wl.Sq - 1]
     for bh in (0, wl.B * wl.H - 1, (wl.B * wl.H) // 2):
         for i in edge:
             if 0 <= i < wl.Sq:
@@ -66,7 +66,7 @@ def _run_config(name):
             rows.add((b, h, i))
     rows = sorted(rows)
     t0 = time.perf_counter()
-    ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows)
+    ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask=wl.mask)
     say(f"  oracle on {len(rows)} rows in {time.perf_counter() - t0:.1f} s")
     dev = Dev(inp)
     outs = {}
@@ -80,7 +80,7 @@ def _run_config(name):
     again = dev.run(wl.modes[0])
     assert np.array_equal(again, outs[wl.modes[0]]), "repeated launch changed the output"
     # the key-range-splitting entry point, where this shape splits
-    if attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
+    if wl.mask == "none" and attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
         for mode in wl.modes:
             out = dev.run(mode, split=True)
             res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
@@ -132,3 +132,15 @@ def test_stressed_logits_with_k_specials():
     assert not np.any(((out & 0x7FFF) == 0x7F80)), "an output element is infinite"
     # the x64-scaled rows were sampled too: make sure some were checked
     say(f"  NaN rows: {int(nan_rows.sum())} of {nan_rows.size}")
+
+
+@pytest.mark.timeout(600)
+def test_causal_self_attention_8k():
+    # B=4 H=16 Sq=Sk=8192 BSHD RTNE, diagonal at the top left
+    _run_config("self8k_causal")
+
+
+@pytest.mark.timeout(600)
+def test_causal_bottom_right_prefill_odd_lengths():
+    # B=2 H=24 Sq=4097 Sk=32771 BSHD RTZ, diagonal at the bottom right: row i sees keys <= i + 28674
+    _run_config("prefill_br")
