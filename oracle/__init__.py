@@ -1,4 +1,5 @@
-"""Plain fp64 CPU oracle for bf16 forward attention (d = 128), unmasked or causal.
+"""Plain fp64 CPU oracle for bf16 forward attention (d = 128), unmasked or causal,
+with as many K/V heads as query heads or fewer (grouped-query attention).
 
 TEST INFRASTRUCTURE ONLY: the test-suite, the smoke check and the CPU-baseline
 leg of the benchmark may import this package; the product path never does.
@@ -22,7 +23,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                        past the diagonal cannot change it, rows with no
                        visible key are NaN, mpmath brute force, and torch's
                        float64 attention with its top-left (``is_causal``) and
-                       bottom-right (``causal_lower_right``) masks.
+                       bottom-right (``causal_lower_right``) masks.  With
+                       fewer K/V heads (read from k's shape): equal, bit for
+                       bit, to the one-head-per-query-head oracle on K/V
+                       heads repeated group-wise, and torch's float64
+                       attention with ``enable_gqa``.
 * ``softmax_row``   -- rows sum to one; agrees with a library softmax.
 """
 from __future__ import annotations
@@ -85,6 +90,9 @@ def _load():
         lib.oracle_attn_rows_masked.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                                 i64p, i64, f64p, u16p, ctypes.c_int]
         lib.oracle_attn_rows_masked.restype = ctypes.c_int
+        lib.oracle_attn_rows_gqa.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                             i64p, i64, f64p, u16p, ctypes.c_int]
+        lib.oracle_attn_rows_gqa.restype = ctypes.c_int
         lib.oracle_softmax_row.argtypes = [u16p, u16p, i64, i64, i64, i64, ctypes.c_int,
                                            i64, i64, i64, f64p]
         lib.oracle_softmax_row.restype = ctypes.c_double
@@ -123,9 +131,11 @@ def round_bf16(x: np.ndarray, mode: str) -> np.ndarray:
     return out
 
 
-def _check_inputs(q, k, v, B, H, Sq, Sk, layout):
+def _check_inputs(q, k, v, B, H, H_kv, Sq, Sk, layout):
+    if H_kv < 1 or H % H_kv:
+        raise ValueError(f"the {H} query heads are not a multiple of the {H_kv} K/V heads")
     shape_q = (B, Sq, H, D) if layout == "bshd" else (B, H, Sq, D)
-    shape_k = (B, Sk, H, D) if layout == "bshd" else (B, H, Sk, D)
+    shape_k = (B, Sk, H_kv, D) if layout == "bshd" else (B, H_kv, Sk, D)
     for name, t, shp in (("q", q, shape_q), ("k", k, shape_k), ("v", v, shape_k)):
         if t.dtype != np.uint16 or tuple(t.shape) != shp or not t.flags.c_contiguous:
             raise ValueError(f"{name}: expected contiguous uint16 {shp}, got {t.dtype} {t.shape}")
@@ -135,19 +145,20 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
               mask: str = "none"):
     """Exact outputs of the given (b, h, i) query rows and their roundings.
 
-    ``q``/``k``/``v`` are bf16 bit arrays stored in ``layout``; ``mask`` is
-    one of ``MASKS``.  Returns
+    ``q``/``k``/``v`` are bf16 bit arrays stored in ``layout`` (k and v may
+    hold fewer heads than q: grouped-query attention); ``mask`` is one of
+    ``MASKS``.  Returns
     ``(o_exact, o_round)``: ``o_exact`` is float64 [n, 128] and ``o_round``
     uint16 [n, 3, 128] in the mode order RTNE, RTNA, RTZ; both follow the
     order of ``rows``.
     """
     if layout == "bshd":
         B, Sq, H, _ = q.shape
-        Sk = k.shape[1]
+        Sk, H_kv = k.shape[1], k.shape[2]
     else:
         B, H, Sq, _ = q.shape
-        Sk = k.shape[2]
-    _check_inputs(q, k, v, B, H, Sq, Sk, layout)
+        H_kv, Sk = k.shape[1], k.shape[2]
+    _check_inputs(q, k, v, B, H, H_kv, Sq, Sk, layout)
     rows = np.asarray(rows, dtype=np.int64).reshape(-1, 3)
     n = rows.shape[0]
     order = np.lexsort((rows[:, 2], rows[:, 1], rows[:, 0]))
@@ -156,9 +167,9 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
     o_round = np.empty((n, 3, D), dtype=np.uint16)
     if mask not in MASKS:
         raise ValueError(f"mask must be one of {sorted(MASKS)}, got {mask!r}")
-    rc = _load().oracle_attn_rows_masked(_u16(q), _u16(k), _u16(v), B, H, Sq, Sk, LAYOUTS[layout], MASKS[mask],
-                                         srt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
-                                         _f64(o_exact), _u16(o_round), nthreads or default_threads())
+    rc = _load().oracle_attn_rows_gqa(_u16(q), _u16(k), _u16(v), B, H, H_kv, Sq, Sk, LAYOUTS[layout], MASKS[mask],
+                                      srt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
+                                      _f64(o_exact), _u16(o_round), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_attn_rows failed with {rc}")
     inv = np.empty_like(order)

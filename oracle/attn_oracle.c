@@ -1,6 +1,6 @@
 /*
  * attn_oracle.c -- plain fp64 CPU oracle for bf16 forward attention, without a
- * mask or with a causal one.
+ * mask or with a causal one, with as many K/V heads as query heads or fewer.
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
  * load this file or the library built from it; only the test-suite, the
@@ -41,6 +41,12 @@
  * the visible keys j < n_i = min(max(i + off + 1, 0), Sk) only.  A row with no
  * visible key has an empty sum, l = 0 and o = 0/0 = NaN, the same result the
  * formula gives when every logit of a row is -Inf.
+ *
+ * Grouped K/V heads.  The same page lists GQA among what the kernel leaves
+ * out (section "Hvad er udgivet" / What was released), again without a
+ * definition.  Read as the usual one: K and V hold H_kv heads, H is a
+ * multiple of H_kv, and query head h attends with K/V head h / (H / H_kv)
+ * (consecutive query heads share one K/V head).  Everything else is as above.
  *
  * Pins (tests/test_oracle_*.py): closed forms, invariants, brute force on
  * tiny inputs, a library softmax cross-check and exhaustive/definitional
@@ -254,7 +260,7 @@ static void *run_job(void *arg)
     return NULL;
 }
 
-/* Decode head (b, h) of a K or V tensor into a dense [S][D] binary64 array. */
+/* Decode head (b, h) of a K or V tensor of H heads into a dense [S][D] binary64 array. */
 static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int64_t b, int64_t h, double *out)
 {
     for (int64_t s = 0; s < S; ++s)
@@ -263,9 +269,10 @@ static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int
 }
 
 /*
- * oracle_attn_rows_masked: exact outputs and their three bf16 roundings for
- * a list of query rows.
- *   q: [B,Sq,H,128] (BSHD) or [B,H,Sq,128] (BHSD) bf16 bits; k, v likewise with Sk.
+ * oracle_attn_rows_gqa: exact outputs and their three bf16 roundings for a
+ * list of query rows.
+ *   q: [B,Sq,H,128] (BSHD) or [B,H,Sq,128] (BHSD) bf16 bits; k, v likewise
+ *   with Sk rows and H_kv heads (H a multiple of H_kv).
  *   mask: OR_MASK_NONE, OR_MASK_CAUSAL_TOP_LEFT or OR_MASK_CAUSAL_BOTTOM_RIGHT.
  *   rows: nrows triples (b, h, i); rows with equal (b, h) must be adjacent.
  *   o_exact: nrows x 128 binary64;  o_round: nrows x 3 x 128 bf16 bits
@@ -273,15 +280,17 @@ static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int
  *   nthreads: worker threads (rows of one head are split among them).
  * Returns 0 on success, -1 on bad arguments, -2 on allocation failure.
  */
-int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
-                            int64_t B, int64_t H, int64_t Sq, int64_t Sk, int layout, int mask,
-                            const int64_t *rows, int64_t nrows,
-                            double *o_exact, uint16_t *o_round, int nthreads)
+int oracle_attn_rows_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int mask,
+                         const int64_t *rows, int64_t nrows,
+                         double *o_exact, uint16_t *o_round, int nthreads)
 {
     if (!q || !k || !v || !rows || !o_exact || !o_round)
         return -1;
-    if (B < 1 || H < 1 || Sq < 1 || Sk < 1 || (layout != OR_BSHD && layout != OR_BHSD))
+    if (B < 1 || H < 1 || H_kv < 1 || H % H_kv != 0 || Sq < 1 || Sk < 1 ||
+        (layout != OR_BSHD && layout != OR_BHSD))
         return -1;
+    const int64_t group = H / H_kv; /* query heads per K/V head */
     if (mask != OR_MASK_NONE && mask != OR_MASK_CAUSAL_TOP_LEFT && mask != OR_MASK_CAUSAL_BOTTOM_RIGHT)
         return -1;
     if (nthreads < 1)
@@ -306,8 +315,8 @@ int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t
         int64_t r1 = r0;
         while (r1 < nrows && rows[3 * r1] == b && rows[3 * r1 + 1] == h)
             ++r1;
-        decode_head(k, layout, H, Sk, b, h, Kd);
-        decode_head(v, layout, H, Sk, b, h, Vd);
+        decode_head(k, layout, H_kv, Sk, b, h / group, Kd);
+        decode_head(v, layout, H_kv, Sk, b, h / group, Vd);
         int64_t n = r1 - r0;
         int nt = (int64_t)nthreads < n ? nthreads : (int)n;
         for (int t = 0; t < nt; ++t) {
@@ -335,6 +344,15 @@ int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t
     }
     free(Kd), free(Vd), free(jobs), free(th);
     return status;
+}
+
+/* oracle_attn_rows_masked: oracle_attn_rows_gqa with one K/V head per query head. */
+int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t *v,
+                            int64_t B, int64_t H, int64_t Sq, int64_t Sk, int layout, int mask,
+                            const int64_t *rows, int64_t nrows,
+                            double *o_exact, uint16_t *o_round, int nthreads)
+{
+    return oracle_attn_rows_gqa(q, k, v, B, H, H, Sq, Sk, layout, mask, rows, nrows, o_exact, o_round, nthreads);
 }
 
 /* oracle_attn_rows: the unmasked case of oracle_attn_rows_masked. */
