@@ -4,8 +4,8 @@
 A step is one call of the library over the whole workload (every query row of
 every head), inputs resident in HBM: attn_fwd_bf16_ws with a preallocated
 workspace when the shape splits its key ranges (then the step is both of its
-kernels), attn_fwd_bf16_masked for the causal workloads, attn_fwd_bf16
-otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
+kernels), attn_fwd_bf16_gqa for the grouped-query workloads,
+attn_fwd_bf16_masked for the causal ones, attn_fwd_bf16 otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
 BSHD, RTNE.  Prints one JSON line:
 
   value      forward TFLOP/s, 4*128 FLOPs per visible (query, key) pair (all
@@ -196,7 +196,9 @@ def main():
     o = torch.empty_like(q)
     stream = torch.cuda.current_stream(dev)
     masked = wl.mask != "none"
-    ws_bytes = 0 if args.no_split or masked else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
+    grouped = wl.kv_heads != wl.H
+    ws_bytes = (0 if args.no_split or masked or grouped
+                else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk))
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
               attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
@@ -205,6 +207,8 @@ def main():
             wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64), torch.cuda.get_device_properties(dev).multi_processor_count)
         entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
                  f"{tps} tiles, {ws_bytes} B workspace")
+    elif grouped:
+        entry = f"attn_fwd_bf16_gqa(H_kv={wl.kv_heads}, {wl.mask})"
     elif masked:
         entry = f"attn_fwd_bf16_masked({wl.mask})"
     else:
@@ -214,6 +218,9 @@ def main():
     def step():
         if ws_bytes > 0:
             st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+        elif grouped:
+            st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], wl.B, wl.H, wl.kv_heads, wl.Sq,
+                                        wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], stream.cuda_stream)
         elif masked:
             st = attn.attn_fwd_bf16_masked(*args_c, attn.MASKS[wl.mask], stream.cuda_stream)
         else:
@@ -261,8 +268,9 @@ def main():
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": f"{wl.name}: B={wl.B} H={wl.H} Sq={wl.Sq} Sk={wl.Sk} d=128 {wl.layout.upper()} "
-                               f"{mode.upper()}" + (f" {wl.mask}" if masked else ""),
-                   "B": wl.B, "H": wl.H, "Sq": wl.Sq, "Sk": wl.Sk,
+                               f"{mode.upper()}" + (f" {wl.mask}" if masked else "")
+                               + (f" H_kv={wl.kv_heads}" if grouped else ""),
+                   "B": wl.B, "H": wl.H, "H_kv": wl.kv_heads, "Sq": wl.Sq, "Sk": wl.Sk,
                    "head_dim": 128, "layout": wl.layout, "round_mode": mode, "mask": wl.mask,
                    "flops_per_step": flops},
         "entry_point": entry,

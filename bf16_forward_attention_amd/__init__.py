@@ -6,6 +6,7 @@ only, every step of the computation runs in the HIP library
 
     attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
     attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream) -> status
+    attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream) -> status
     attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
     attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
@@ -17,7 +18,7 @@ import ctypes
 import os
 
 __all__ = [
-    "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size",
+    "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_gqa", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size",
     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
     "AttnError", "LAYOUTS", "ROUND_MODES", "MASKS", "library_path", "load_library",
 ]
@@ -60,6 +61,9 @@ def load_library():
         lib.attn_fwd_bf16_masked.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, vp]
         lib.attn_fwd_bf16_masked.restype = ctypes.c_int
+        lib.attn_fwd_bf16_gqa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                                          ctypes.c_int, vp]
+        lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
         lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
                                          vp]
         lib.attn_fwd_bf16_ws.restype = ctypes.c_int
@@ -85,6 +89,12 @@ def attn_fwd_bf16_masked(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int
                          layout: int, round_mode: int, mask: int, stream: int) -> int:
     """The masked C entry point with raw device addresses; returns the status code."""
     return load_library().attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream)
+
+
+def attn_fwd_bf16_gqa(q: int, k: int, v: int, o: int, B: int, H: int, H_kv: int, Sq: int, Sk: int,
+                      layout: int, round_mode: int, mask: int, stream: int) -> int:
+    """The grouped-query C entry point with raw device addresses; returns the status code."""
+    return load_library().attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream)
 
 
 def attn_fwd_bf16_ws(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int, layout: int,
@@ -129,17 +139,19 @@ def _dims(q, k, layout: str):
         Bk, Hk, Sk, dk = k.shape
     else:
         raise ValueError(f"layout must be one of {sorted(LAYOUTS)}, got {layout!r}")
-    if d != HEAD_DIM or dk != HEAD_DIM or Bk != B or Hk != H:
+    if d != HEAD_DIM or dk != HEAD_DIM or Bk != B or Hk < 1 or H % Hk:
         raise ValueError(f"incompatible shapes q{tuple(q.shape)} k{tuple(k.shape)} for layout {layout}")
-    return B, H, Sq, Sk
+    return B, H, Hk, Sq, Sk
 
 
 def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None,
              split: bool = True, mask: str = "none"):
     """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
 
-    ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H,128] for "bshd", or
-    [B,H,S,128] for "bhsd"; all contiguous bf16 on one device.  Enqueued on
+    ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H_kv,128] for "bshd", or
+    [B,H,S,128] / [B,H_kv,S,128] for "bhsd"; all contiguous bf16 on one
+    device.  H_kv < H (a divisor of H) is grouped-query attention through
+    attn_fwd_bf16_gqa.  Enqueued on
     ``stream`` (default: torch's current stream on that device).  With
     ``split`` the key range may be split (attn_fwd_bf16_ws, workspace from
     torch); without, the single-pass attn_fwd_bf16.  ``mask`` "causal" or
@@ -152,7 +164,7 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         raise ValueError(f"round_mode must be one of {sorted(ROUND_MODES)}, got {round_mode!r}")
     if mask not in MASKS:
         raise ValueError(f"mask must be one of {sorted(MASKS)}, got {mask!r}")
-    B, H, Sq, Sk = _dims(q, k, layout)
+    B, H, H_kv, Sq, Sk = _dims(q, k, layout)
     if tuple(v.shape) != tuple(k.shape):
         raise ValueError("v must have the shape of k")
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -167,8 +179,11 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and mask == "none" else 0
-        if mask != "none":
+        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and mask == "none" and H_kv == H else 0
+        if H_kv != H:
+            status = attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, H_kv, Sq,
+                                       Sk, LAYOUTS[layout], ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
+        elif mask != "none":
             status = attn_fwd_bf16_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
                                           LAYOUTS[layout], ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
         elif ws_bytes > 0:

@@ -120,6 +120,7 @@ struct Geometry {
   int64_t k_head;
   int64_t q_batch; // element offset of batch b
   int64_t k_batch;
+  int64_t kv_group; // query heads per K/V head: query head h reads K/V head h / kv_group
 };
 
 // Work items are (b, h, q-tile) in row-major order.  Items [0, n_whole) run
@@ -244,8 +245,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   const int grp = lane >> 5;
 
   const uint16_t* Qh = Q + b * g.q_batch + h * g.q_head;
-  const uint16_t* Kh = K + b * g.k_batch + h * g.k_head;
-  const uint16_t* Vh = V + b * g.k_batch + h * g.k_head;
+  const int hk = h / (int)g.kv_group;
+  const uint16_t* Kh = K + b * g.k_batch + hk * g.k_head;
+  const uint16_t* Vh = V + b * g.k_batch + hk * g.k_head;
   uint16_t* Oh = O + b * g.q_batch + h * g.q_head;
   const uint32_t row_bytes = (uint32_t)(g.k_row * 2);
 
@@ -738,13 +740,14 @@ struct Problem {
   int64_t bytes_q, bytes_k, n_work, n_qtiles, n_tiles;
 };
 // argument checks shared by the entry points (no HIP calls)
-int check_args(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t H, int64_t Sq,
-               int64_t Sk, int layout, int round_mode, Problem* pb) {
+int check_args(const void* q, const void* k, const void* v, const void* o, int64_t B, int64_t H, int64_t H_kv,
+               int64_t Sq, int64_t Sk, int layout, int round_mode, Problem* pb) {
   if (!q || !k || !v || !o) return ATTN_ERR_NULL;
-  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SIZE;
-  int64_t bh, nq, nk;
-  if (!mul_ok(B, H, &bh) || !mul_ok(bh, Sq, &nq) || !mul_ok(nq, 2 * D, &pb->bytes_q) || !mul_ok(bh, Sk, &nk) ||
-      !mul_ok(nk, 2 * D, &pb->bytes_k))
+  if (B < 1 || H < 1 || H_kv < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SIZE;
+  if (H % H_kv != 0) return ATTN_ERR_HEADS;
+  int64_t bh, bhk, nq, nk;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, Sq, &nq) || !mul_ok(nq, 2 * D, &pb->bytes_q) || !mul_ok(B, H_kv, &bhk) ||
+      !mul_ok(bhk, Sk, &nk) || !mul_ok(nk, 2 * D, &pb->bytes_k))
     return ATTN_ERR_SIZE;
   pb->n_qtiles = (Sq + BM - 1) / BM;
   pb->n_tiles = (Sk + BN - 1) / BN;
@@ -762,23 +765,24 @@ int check_args(const void* q, const void* k, const void* v, const void* o, int64
   return ATTN_OK;
 }
 
-Geometry make_geometry(int64_t H, int64_t Sq, int64_t Sk, int layout) {
+Geometry make_geometry(int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout) {
   Geometry g;
   if (layout == ATTN_LAYOUT_BSHD) {
     g.q_row = H * D;
-    g.k_row = H * D;
+    g.k_row = H_kv * D;
     g.q_head = D;
     g.k_head = D;
     g.q_batch = Sq * H * D;
-    g.k_batch = Sk * H * D;
+    g.k_batch = Sk * H_kv * D;
   } else {
     g.q_row = D;
     g.k_row = D;
     g.q_head = Sq * D;
     g.k_head = Sk * D;
     g.q_batch = H * Sq * D;
-    g.k_batch = H * Sk * D;
+    g.k_batch = H_kv * Sk * D;
   }
+  g.kv_group = H / H_kv;
   return g;
 }
 
@@ -803,9 +807,9 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
   }
 }
 
-int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t Sq, int64_t Sk, int layout,
-        int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
-  const Geometry g = make_geometry(H, Sq, Sk, layout);
+int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
+        int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
+  const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
   Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
   if (plan.n_split_items > 0) {
     sp.part = (float*)workspace;
@@ -838,19 +842,20 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
 extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                              int64_t Sq, int64_t Sk, int layout, int round_mode, void* stream) {
   Problem pb;
-  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  const int st = check_args(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
   int n_cu = 0;
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream);
+  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream);
 }
 
-extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
-                                    int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* stream) {
+extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                                 int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode, int mask,
+                                 void* stream) {
   Problem pb;
-  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  const int st = check_args(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_MASK;
@@ -858,7 +863,12 @@ extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v,
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream);
+  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream);
+}
+
+extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
+                                    int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* stream) {
+  return attn_fwd_bf16_gqa(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, mask, stream);
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {
@@ -891,7 +901,7 @@ extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, voi
                                 int64_t Sq, int64_t Sk, int layout, int round_mode, void* workspace,
                                 int64_t workspace_bytes, void* stream) {
   Problem pb;
-  const int st = check_args(q, k, v, o, B, H, Sq, Sk, layout, round_mode, &pb);
+  const int st = check_args(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
   if (workspace_bytes < 0) return ATTN_ERR_SIZE;
   int n_cu = 0;
@@ -907,7 +917,7 @@ extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, voi
         overlaps(workspace, need, v, pb.bytes_k) || overlaps(workspace, need, o, pb.bytes_q))
       return ATTN_ERR_ALIAS;
   }
-  return run(q, k, v, o, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, plan, workspace, stream);
+  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, plan, workspace, stream);
 }
 
 extern "C" const char* attn_fwd_bf16_strerror(int status) {
@@ -923,6 +933,7 @@ extern "C" const char* attn_fwd_bf16_strerror(int status) {
     case ATTN_ERR_HIP: return "the HIP kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_bf16_workspace_size reports";
     case ATTN_ERR_MASK: return "mask is not an attn_mask_t value";
+    case ATTN_ERR_HEADS: return "the query head count is not a multiple of the K/V head count";
     default: return "unknown status";
   }
 }

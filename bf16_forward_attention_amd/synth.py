@@ -226,6 +226,11 @@ class Workload:
     checked_rows_per_head: int = 0  # 0: every row is checkable
     seed: int = 0
     mask: str = "none"  # key mask the workload is run with: "none", "causal", "causal_br"
+    H_kv: int = 0  # K/V heads (grouped-query attention); 0: as many as query heads
+
+    @property
+    def kv_heads(self) -> int:
+        return self.H_kv or self.H
 
     @property
     def flops(self) -> int:
@@ -246,6 +251,8 @@ WORKLOADS = {
     # against a longer key cache (diagonal at the bottom right, ragged tiles)
     "self8k_causal": Workload("self8k_causal", 4, 16, 8192, 8192, "bshd", ("rtne",), mask="causal"),
     "prefill_br": Workload("prefill_br", 2, 24, 4097, 32771, "bshd", ("rtz",), mask="causal_br"),
+    # grouped-query causal prefill: 32 query heads over 8 K/V heads
+    "gqa8k_causal": Workload("gqa8k_causal", 2, 32, 8192, 8192, "bshd", ("rtne",), mask="causal", H_kv=8),
 }
 
 
@@ -271,7 +278,7 @@ def special_list(wl: Workload) -> list[tuple]:
     """Three K specials (NaN, +Inf, -Inf) in three distinct (b, h) heads."""
     if not wl.inject_k_specials:
         return []
-    heads = floyd_sample(wl.seed, TID_SPECIAL, wl.B * wl.H, 3, stream=0)
+    heads = floyd_sample(wl.seed, TID_SPECIAL, wl.B * wl.kv_heads, 3, stream=0)
     key = stream_key(wl.seed, TID_SPECIAL)
     order = [u64_int(key, (1 << 32) + t) for t in range(3)]
     # shuffle which head gets which special, deterministically
@@ -280,7 +287,7 @@ def special_list(wl: Workload) -> list[tuple]:
     for t, (bits, bh) in enumerate(zip((BF16_NAN, BF16_PINF, BF16_NINF), heads)):
         j = (u64_int(key, (2 << 32) + t) * wl.Sk) >> 64
         c = (u64_int(key, (3 << 32) + t) * D) >> 64
-        out.append((bits, bh // wl.H, bh % wl.H, int(j), int(c)))
+        out.append((bits, bh // wl.kv_heads, bh % wl.kv_heads, int(j), int(c)))
     return out
 
 
@@ -304,16 +311,16 @@ def checked_rows(wl: Workload) -> list[tuple]:
 def generate(wl: Workload) -> Inputs:
     """Draw Q, K, V for ``wl`` and store them in ``wl.layout``."""
     nq = wl.B * wl.H * wl.Sq * D
-    nk = wl.B * wl.H * wl.Sk * D
+    nk = wl.B * wl.kv_heads * wl.Sk * D
     q = normal_bf16(wl.seed, TID_Q, nq, wl.qk_sigma).reshape(wl.B, wl.H, wl.Sq, D)
-    k = normal_bf16(wl.seed, TID_K, nk, wl.qk_sigma).reshape(wl.B, wl.H, wl.Sk, D)
+    k = normal_bf16(wl.seed, TID_K, nk, wl.qk_sigma).reshape(wl.B, wl.kv_heads, wl.Sk, D)
     if wl.v_dist == "normal":
         v = normal_bf16(wl.seed, TID_V, nk, 1.0)
     elif wl.v_dist == "uniform":
         v = uniform_bf16(wl.seed, TID_V, nk, -1.0, 1.0)
     else:
         raise ValueError(wl.v_dist)
-    v = v.reshape(wl.B, wl.H, wl.Sk, D)
+    v = v.reshape(wl.B, wl.kv_heads, wl.Sk, D)
 
     rows = scaled_row_list(wl)
     if rows:
@@ -331,8 +338,8 @@ def generate(wl: Workload) -> Inputs:
 
 
 def small(B: int, H: int, Sq: int, Sk: int, layout: str = "bshd", seed: int = 0,
-          qk_sigma: float = 1.0, v_dist: str = "normal", mask: str = "none") -> Inputs:
+          qk_sigma: float = 1.0, v_dist: str = "normal", mask: str = "none", H_kv: int = 0) -> Inputs:
     """A small i.i.d. workload for parity tests."""
-    wl = Workload(f"small_{B}x{H}x{Sq}x{Sk}_{layout}_{mask}", B, H, Sq, Sk, layout, MODES,
-                  qk_sigma=qk_sigma, v_dist=v_dist, seed=seed, mask=mask)
+    wl = Workload(f"small_{B}x{H}x{H_kv or H}x{Sq}x{Sk}_{layout}_{mask}", B, H, Sq, Sk, layout, MODES,
+                  qk_sigma=qk_sigma, v_dist=v_dist, seed=seed, mask=mask, H_kv=H_kv)
     return generate(wl)

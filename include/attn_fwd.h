@@ -8,7 +8,8 @@
  *     O[b,h,i,:] = softmax_j( Q[b,h,i,:] . K[b,h,j,:] / sqrt(128) ) V[b,h,j,:]
  *
  * without a mask (attn_fwd_bf16_masked adds a causal one), head_dim fixed at
- * 128, one head count shared by Q, K and V, any
+ * 128, one head count shared by Q, K and V (attn_fwd_bf16_gqa allows fewer
+ * K/V heads), any
  * query length Sq and key length Sk (cross-attention allowed), inputs read in
  * the BSHD or BHSD layout without a transpose (same page, section "Hvad er
  * udgivet" / What was released).  Output is bf16, rounded per call in one of
@@ -44,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 3
+#define ATTN_FWD_ABI_VERSION 4
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -76,7 +77,8 @@ typedef enum {
     ATTN_ERR_DEVICE = 7, /* the current device is not gfx950, or cannot be queried */
     ATTN_ERR_HIP = 8,    /* the kernel launch failed */
     ATTN_ERR_WORKSPACE = 9, /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
-    ATTN_ERR_MASK = 10      /* mask is not an attn_mask_t value */
+    ATTN_ERR_MASK = 10,     /* mask is not an attn_mask_t value */
+    ATTN_ERR_HEADS = 11     /* H is not a multiple of H_kv */
 } attn_status_t;
 
 /*
@@ -160,6 +162,30 @@ int attn_fwd_bf16_ws(const void *q, const void *k, const void *v, void *o,
 int attn_fwd_bf16_masked(const void *q, const void *k, const void *v, void *o,
                          int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                          int layout, int round_mode, int mask, void *stream);
+
+/*
+ * attn_fwd_bf16_gqa -- attn_fwd_bf16_masked with fewer K/V heads than query
+ * heads (grouped-query attention).
+ *
+ * The snilld.dk page lists GQA among what the kernel it describes leaves out
+ * (section "Hvad er udgivet" / What was released) without defining it; this
+ * is the usual grouping.  K and V hold H_kv heads, H must be a multiple of
+ * H_kv, and query head h attends with K/V head h / (H / H_kv), so
+ * consecutive query heads share one K/V head (H_kv = 1: multi-query
+ * attention; H_kv = H: attn_fwd_bf16_masked).
+ *
+ *   q, o    : [B, Sq, H, 128] (BSHD) or [B, H, Sq, 128] (BHSD).
+ *   k, v    : [B, Sk, H_kv, 128] (BSHD) or [B, H_kv, Sk, 128] (BHSD).
+ *   H_kv    : K/V head count, >= 1, dividing H.
+ *   mask    : attn_mask_t, as attn_fwd_bf16_masked.
+ *   other arguments : as attn_fwd_bf16.
+ *
+ * Status codes as attn_fwd_bf16_masked, plus ATTN_ERR_HEADS (H not a
+ * multiple of H_kv; H_kv < 1 is ATTN_ERR_SIZE).
+ */
+int attn_fwd_bf16_gqa(const void *q, const void *k, const void *v, void *o,
+                      int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
+                      int layout, int round_mode, int mask, void *stream);
 
 /*
  * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs

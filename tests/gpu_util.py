@@ -58,6 +58,22 @@ def launch_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
         raise attn.AttnError(st)
 
 
+def launch_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
+               mask: str = "none", stream: torch.cuda.Stream | None = None) -> None:
+    """Call attn_fwd_bf16_gqa through the C ABI; the K/V head count comes from k's shape."""
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Sk, H_kv = k.shape[1], k.shape[2]
+    else:
+        B, H, Sq, _ = q.shape
+        H_kv, Sk = k.shape[1], k.shape[2]
+    s = stream if stream is not None else torch.cuda.current_stream()
+    st = attn.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, H_kv, Sq, Sk,
+                                attn.LAYOUTS[layout], attn.ROUND_MODES[mode], attn.MASKS[mask], s.cuda_stream)
+    if st != 0:
+        raise attn.AttnError(st)
+
+
 def launch_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
               stream: torch.cuda.Stream | None = None) -> int:
     """Call attn_fwd_bf16_ws (key ranges split when it pays) with a torch-allocated
@@ -92,7 +108,9 @@ class Dev:
         """Output bits in the stored layout (split: through attn_fwd_bf16_ws; a
         mask, or the workload's own, through attn_fwd_bf16_masked)."""
         mask = self.inp.wl.mask if mask is None else mask
-        if mask != "none":
+        if self.inp.wl.kv_heads != self.inp.wl.H:
+            launch_gqa(self.q, self.k, self.v, self.o, self.layout, mode, mask)
+        elif mask != "none":
             launch_masked(self.q, self.k, self.v, self.o, self.layout, mode, mask)
         elif split:
             launch_ws(self.q, self.k, self.v, self.o, self.layout, mode)

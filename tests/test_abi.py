@@ -25,8 +25,9 @@ def _enum_values():
 
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
-    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_masked", "attn_fwd_bf16_split_plan",
-                     "attn_fwd_bf16_strerror", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_masked",
+                     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_workspace_size",
+                     "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
@@ -94,12 +95,41 @@ def test_masked_argument_errors_before_any_hip_call(args, code):
     assert attn.attn_fwd_bf16_masked(*args, 0) == ev[code]
 
 
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 1, 4, 2, 1, 1, 0, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 1, 4, 0, 1, 1, 0, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 4, -2, 1, 1, 0, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, 4, 3, 1, 1, 0, 0, 0), "ATTN_ERR_HEADS"),
+    ((A, B_, C, O_, 1, 2, 4, 1, 1, 0, 0, 0), "ATTN_ERR_HEADS"),
+    ((A, B_, C, O_, 1, 4, 2, 1, 1, 9, 0, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 1, 4, 2, 1, 1, 0, 5, 0), "ATTN_ERR_ROUND"),
+    ((A, B_, C + 4, O_, 1, 4, 2, 1, 1, 0, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, C, 1, 4, 2, 1, 1, 0, 0, 0), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, O_, 1, 4, 2, 1, 1, 0, 0, 7), "ATTN_ERR_MASK"),
+])
+def test_gqa_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_gqa(*args, 0) == ev[code]
+
+
+def test_gqa_alias_check_uses_the_kv_head_count():
+    # k holds B*H_kv*Sk rows of 256 B: with H_kv = 1, o placed right after k does not overlap it
+    ev = _enum_values()
+    k_bytes = 1 * 1 * 8 * 256
+    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes, 1, 4, 1, 1, 8, 0, 0, 7, 0) == ev["ATTN_ERR_MASK"]
+    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes - 256, 1, 4, 1, 1, 8, 0, 0, 0, 0) == ev["ATTN_ERR_ALIAS"]
+
+
 def test_binding_rejects_unknown_mask_name():
     import torch
 
     q = torch.zeros(1, 1, 1, 128, dtype=torch.bfloat16)
     with pytest.raises(ValueError):
         attn.attn_fwd(q, q, q, mask="upper")
+    k3 = torch.zeros(1, 1, 3, 128, dtype=torch.bfloat16)
+    q4 = torch.zeros(1, 1, 4, 128, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):  # 4 query heads over 3 K/V heads
+        attn.attn_fwd(q4, k3, k3)
 
 
 def test_binding_rejects_missing_library(monkeypatch, tmp_path):

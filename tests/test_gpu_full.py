@@ -80,7 +80,7 @@ def _run_config(name):
     again = dev.run(wl.modes[0])
     assert np.array_equal(again, outs[wl.modes[0]]), "repeated launch changed the output"
     # the key-range-splitting entry point, where this shape splits
-    if wl.mask == "none" and attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
+    if wl.mask == "none" and wl.kv_heads == wl.H and attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
         for mode in wl.modes:
             out = dev.run(mode, split=True)
             res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
@@ -144,3 +144,9 @@ def test_causal_self_attention_8k():
 def test_causal_bottom_right_prefill_odd_lengths():
     # B=2 H=24 Sq=4097 Sk=32771 BSHD RTZ, diagonal at the bottom right: row i sees keys <= i + 28674
     _run_config("prefill_br")
+
+
+@pytest.mark.timeout(600)
+def test_grouped_query_causal_8k():
+    # B=2 H=32 H_kv=8 Sq=Sk=8192 BSHD RTNE, causal: query head h uses K/V head h / 4
+    _run_config("gqa8k_causal")
