@@ -40,6 +40,7 @@ _M2 = np.uint64(0x94D049BB133111EB)
 _MASK64 = (1 << 64) - 1
 
 TID_Q, TID_K, TID_V, TID_ROWSCALE, TID_SPECIAL, TID_SUBSET = 0, 1, 2, 3, 4, 5
+TID_LENGTHS = 6  # sequence lengths of the variable-length batches
 
 LAYOUTS = ("bshd", "bhsd")
 MODES = ("rtne", "rtna", "rtz")
@@ -343,3 +344,59 @@ def small(B: int, H: int, Sq: int, Sk: int, layout: str = "bshd", seed: int = 0,
     wl = Workload(f"small_{B}x{H}x{H_kv or H}x{Sq}x{Sk}_{layout}_{mask}", B, H, Sq, Sk, layout, MODES,
                   qk_sigma=qk_sigma, v_dist=v_dist, seed=seed, mask=mask, H_kv=H_kv)
     return generate(wl)
+
+
+# --------------------------------------------------------------------------
+# variable-length batches (sequences packed one after another)
+# --------------------------------------------------------------------------
+@dataclass(frozen=True)
+class VarlenWorkload:
+    name: str
+    lengths_q: tuple  # query rows of each sequence
+    lengths_k: tuple  # key rows of each sequence
+    H: int
+    H_kv: int
+    modes: tuple
+    mask: str = "none"
+    seed: int = 0
+
+    @property
+    def B(self) -> int:
+        return len(self.lengths_q)
+
+
+@dataclass
+class VarlenInputs:
+    wl: VarlenWorkload
+    q: np.ndarray  # uint16 bf16 bits [total_q, H, 128]
+    k: np.ndarray  # [total_k, H_kv, 128]
+    v: np.ndarray
+    cu_q: np.ndarray  # int32 [B + 1]: sequence b holds packed rows cu[b] .. cu[b+1]-1
+    cu_k: np.ndarray
+
+
+def seeded_lengths(seed: int, n: int, lo: int, hi: int, stream: int = 0) -> tuple:
+    """``n`` lengths uniform in [lo, hi] from the counter-based generator."""
+    key = stream_key(seed, TID_LENGTHS)
+    return tuple(lo + (u64_int(key, (stream << 32) + i) * (hi - lo + 1) >> 64) for i in range(n))
+
+
+def generate_varlen(wl: VarlenWorkload) -> VarlenInputs:
+    """Draw packed Q, K, V for ``wl``: element (t, h, c) of the packed tensor is
+    element (0, t, h, c) of a B=1 BSHD draw of the same generator."""
+    if len(wl.lengths_k) != len(wl.lengths_q) or wl.H % wl.H_kv:
+        raise ValueError("lengths_q and lengths_k differ in count, or H is not a multiple of H_kv")
+    cu_q = np.concatenate([[0], np.cumsum(wl.lengths_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(wl.lengths_k)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    q = normal_bf16(wl.seed, TID_Q, max(tq, 1) * wl.H * D).reshape(-1, wl.H, D)[:tq]
+    k = normal_bf16(wl.seed, TID_K, max(tk, 1) * wl.H_kv * D).reshape(-1, wl.H_kv, D)[:tk]
+    v = normal_bf16(wl.seed, TID_V, max(tk, 1) * wl.H_kv * D).reshape(-1, wl.H_kv, D)[:tk]
+    return VarlenInputs(wl, np.ascontiguousarray(q), np.ascontiguousarray(k), np.ascontiguousarray(v), cu_q, cu_k)
+
+
+VARLEN_WORKLOADS = {
+    # 16 causal sequences of 256 .. 8192 tokens (about 66K in all), 32 query heads over 8 K/V heads
+    "varlen_mix": VarlenWorkload("varlen_mix", seeded_lengths(0, 16, 256, 8192), seeded_lengths(0, 16, 256, 8192),
+                                 32, 8, ("rtne",), mask="causal"),
+}

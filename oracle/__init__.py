@@ -28,6 +28,11 @@ Parity status of each function (what pins it, in ``tests/test_oracle_*.py``):
                        bit, to the one-head-per-query-head oracle on K/V
                        heads repeated group-wise, and torch's float64
                        attention with ``enable_gqa``.
+* ``attn_rows_varlen`` -- sequences packed one after another: each is the
+                       fixed-length attention above on its own rows.  Pinned
+                       by torch's float64 attention run per sequence, a
+                       dominant key per sequence (catches rows or keys taken
+                       from a neighbour), and mutants of the slicing.
 * ``softmax_row``   -- rows sum to one; agrees with a library softmax.
 """
 from __future__ import annotations
@@ -202,3 +207,51 @@ def softmax_row(q, k, layout: str, b: int, h: int, i: int):
     w = np.empty(Sk, dtype=np.float64)
     l = _load().oracle_softmax_row(_u16(q), _u16(k), B, H, Sq, Sk, LAYOUTS[layout], b, h, i, _f64(w))
     return w, l
+
+
+def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, rows, mask: str = "none",
+                     nthreads: int | None = None):
+    """Exact outputs of packed query rows of a variable-length batch.
+
+    ``q`` is [total_q, H, 128] and ``k``/``v`` [total_k, H_kv, 128] bf16 bits:
+    sequence b holds query rows cu_q[b] .. cu_q[b+1]-1 and key rows
+    cu_k[b] .. cu_k[b+1]-1, and attends only within itself (the survey's
+    variable-length batching: FlashAttention's packed "cu_seqlens" layout).
+    Each sequence is the fixed-length problem B=1, Sq = its query rows, Sk = its
+    key rows in BSHD, handed to ``attn_rows`` as such; a sequence with no key
+    gives NaN rows (the 0/0 of an empty softmax).  ``rows`` are (t, h) pairs
+    of packed query row and head.  Returns ``(o_exact, o_round)`` like
+    ``attn_rows``.
+    """
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_k = np.asarray(cu_k, dtype=np.int64)
+    B = len(cu_q) - 1
+    if len(cu_k) != B + 1 or cu_q[0] != 0 or cu_k[0] != 0 or np.any(np.diff(cu_q) < 0) or np.any(np.diff(cu_k) < 0):
+        raise ValueError("cu_q / cu_k must be non-decreasing offsets starting at 0, one more than the sequences")
+    if cu_q[-1] != q.shape[0] or cu_k[-1] != k.shape[0] or v.shape != k.shape:
+        raise ValueError("the offsets do not cover the packed tensors")
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1, 2)
+    n = rows.shape[0]
+    o_exact = np.full((n, D), np.nan)
+    o_round = np.full((n, 3, D), 0x7FC0, dtype=np.uint16)
+    seq = np.searchsorted(cu_q, rows[:, 0], side="right") - 1
+    for b in np.unique(seq):
+        sel = np.nonzero(seq == b)[0]
+        q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+        if k1 == k0:
+            continue  # no key: NaN rows
+        sub = [(0, int(h), int(t - q0)) for t, h in rows[sel]]
+        ex, rd = attn_rows(np.ascontiguousarray(q[q0:q1][None]), np.ascontiguousarray(k[k0:k1][None]),
+                           np.ascontiguousarray(v[k0:k1][None]), "bshd", sub, nthreads, mask)
+        o_exact[sel] = ex
+        o_round[sel] = rd
+    return o_exact, o_round
+
+
+def attn_all_varlen(q, k, v, cu_q, cu_k, mask: str = "none", nthreads: int | None = None):
+    """Every packed row: o_exact [total_q, H, 128] and o_round [3, total_q, H, 128]."""
+    total_q, H, _ = q.shape
+    tt, hh = np.meshgrid(np.arange(total_q), np.arange(H), indexing="ij")
+    rows = np.stack([tt.ravel(), hh.ravel()], axis=1)
+    ex, rd = attn_rows_varlen(q, k, v, cu_q, cu_k, rows, mask, nthreads)
+    return ex.reshape(total_q, H, D), np.moveaxis(rd.reshape(total_q, H, 3, D), 2, 0)

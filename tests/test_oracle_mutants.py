@@ -56,3 +56,44 @@ def test_mutant_is_caught(name, tmp_path):
                         "tests/test_oracle_gqa.py", "tests/test_oracle_rounding.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
+
+
+# Planted mistakes in the Python side of the oracle (the variable-length
+# composition): a copy of the oracle package with one edit is put first on
+# the import path, the C library stays the real one, and the varlen pins run
+# against it.
+PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
+PY_MUTANTS = {
+    "varlen_keys_shifted": ("np.ascontiguousarray(k[k0:k1][None]),\n                           np.ascontiguousarray(v[k0:k1][None])",
+                            "np.ascontiguousarray(k[k0 + 1:k1 + 1][None]),\n                           np.ascontiguousarray(v[k0 + 1:k1 + 1][None])"),
+    "varlen_queries_of_next_sequence": ("q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]",
+                                        "q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[min(b + 1, B - 1)], cu_k[min(b + 2, B)]"),
+    "varlen_empty_keys_zero": ("o_exact = np.full((n, D), np.nan)", "o_exact = np.zeros((n, D))"),
+    "varlen_row_sequence_search": ('seq = np.searchsorted(cu_q, rows[:, 0], side="right") - 1',
+                                   'seq = np.searchsorted(cu_q, rows[:, 0], side="left") - 1'),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PY_MUTANTS) + ["unmutated"])
+def test_python_mutant_is_caught(name, tmp_path):
+    import oracle
+
+    old, new = PY_MUTANTS.get(name, ("", ""))
+    src = open(PY_SRC).read()
+    assert name == "unmutated" or src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    pkg = tmp_path / "oracle"
+    pkg.mkdir()
+    (pkg / "__init__.py").write_text(src.replace(old, new))
+    env = dict(os.environ, ORACLE_LIB=oracle.build())
+    # import the mutant first: the tests then find it in sys.modules whatever
+    # pytest puts on the path
+    boot = ("import sys; sys.path.insert(0, sys.argv[1]); import oracle; "
+            "assert oracle.__file__.startswith(sys.argv[1]), oracle.__file__; import pytest; "
+            "sys.exit(pytest.main(['-x', '-q', '-p', 'no:cacheprovider', 'tests/test_oracle_varlen.py']))")
+    r = subprocess.run([sys.executable, "-c", boot, str(tmp_path)], cwd=ROOT, env=env, capture_output=True, text=True,
+                       timeout=600)
+    assert "AssertionError: /" not in r.stderr, r.stderr[-2000:]
+    if name == "unmutated":  # the harness itself: an exact copy passes
+        assert r.returncode == 0, r.stdout[-2000:]
+    else:
+        assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
