@@ -183,6 +183,9 @@ def main():
     import bf16_forward_attention_amd as attn
     from bf16_forward_attention_amd import synth
 
+    if args.workload in synth.VARLEN_WORKLOADS:
+        main_varlen(args)
+        return
     wl = synth.WORKLOADS[args.workload]
     mode = args.mode or wl.modes[0]
     attn.load_library()
@@ -296,6 +299,118 @@ def main():
         result["parity"] = {"rows": len(rows), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
                             "strict_ulp_hist": res.strict_hist}
         log(f"[bench] parity {res.summary()}")
+    print(json.dumps(result), flush=True)
+
+
+def varlen_visible_pairs(wl) -> np.ndarray:
+    """Visible (query, key) pairs of each sequence of a variable-length workload."""
+    out = []
+    for Sq, Sk in zip(wl.lengths_q, wl.lengths_k):
+        i = np.arange(Sq, dtype=np.int64)
+        if wl.mask == "none":
+            out.append(Sq * Sk)
+        else:
+            off = 0 if wl.mask == "causal" else Sk - Sq
+            out.append(int(np.clip(i + off + 1, 0, Sk).sum()))
+    return np.array(out, dtype=np.int64)
+
+
+def main_varlen(args):
+    """The same protocol for a packed variable-length batch (attn_fwd_bf16_varlen)."""
+    import torch
+
+    import bf16_forward_attention_amd as attn
+    from bf16_forward_attention_amd import synth
+
+    wl = synth.VARLEN_WORKLOADS[args.workload]
+    mode = args.mode or wl.modes[0]
+    attn.load_library()
+    dev = torch.device("cuda:0")
+    log(f"[bench] generating {wl.name}: {wl.B} sequences, {sum(wl.lengths_q)} query / {sum(wl.lengths_k)} key rows")
+    inp = synth.generate_varlen(wl)
+    t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = t(inp.q), t(inp.k), t(inp.v)
+    cq, ck = torch.from_numpy(inp.cu_q).to(dev), torch.from_numpy(inp.cu_k).to(dev)
+    o = torch.empty_like(q)
+    stream = torch.cuda.current_stream(dev)
+    max_q = max(wl.lengths_q)
+    entry = f"attn_fwd_bf16_varlen(B={wl.B}, H_kv={wl.H_kv}, {wl.mask})"
+    log(f"[bench] entry point: {entry}")
+
+    def step():
+        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+                                       ck.data_ptr(), wl.B, wl.H, wl.H_kv, q.shape[0], k.shape[0], max_q,
+                                       attn.ROUND_MODES[mode], attn.MASKS[wl.mask], stream.cuda_stream)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    ms_per_step = starts[0].elapsed_time(ends[-1]) / args.steps
+    flops = 4.0 * 128 * wl.H * float(varlen_visible_pairs(wl).sum())
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (per.mean() * 1e-3) / 1e12
+    log(f"[bench] {ms_per_step:.3f} ms/step, per-launch mean {per.mean():.3f} median {np.median(per):.3f} ms "
+        f"-> {value:.1f} TFLOP/s")
+    out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
+    result = {
+        "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.B} packed sequences of {min(wl.lengths_q)}..{max(wl.lengths_q)} "
+                               f"tokens ({sum(wl.lengths_q)} in all), H={wl.H} H_kv={wl.H_kv} d=128 "
+                               f"{mode.upper()} {wl.mask}",
+                   "lengths_q": list(wl.lengths_q), "lengths_k": list(wl.lengths_k), "H": wl.H, "H_kv": wl.H_kv,
+                   "head_dim": 128, "round_mode": mode, "mask": wl.mask, "flops_per_step": flops},
+        "entry_point": entry,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                     "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                     "traffic": measured_traffic(wl.name),
+                     "kernel": f"attn_fwd_kernel<{mode.upper()}, varlen{', causal' if wl.mask != 'none' else ''}>",
+                     "launch_ms_mean": round(float(per.mean()), 4),
+                     "launch_ms_median": round(float(np.median(per)), 4)},
+    }
+    if not args.no_cpu_baseline:
+        import oracle
+        from tests.gate import gate
+
+        total_q = q.shape[0]
+        flat = synth.floyd_sample(wl.seed, synth.TID_SUBSET, total_q * wl.H, min(args.parity_rows, total_q * wl.H),
+                                  stream=(1 << 20) + 2)
+        rows = [(f // wl.H, f % wl.H) for f in flat]
+        ex, rd = oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows, wl.mask)
+        got = np.stack([out_bits[t_, h] for t_, h in rows])
+        res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)
+        result["parity"] = {"rows": len(rows), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
+                            "strict_ulp_hist": res.strict_hist}
+        log(f"[bench] parity {res.summary()}")
+        # CPU baseline: the oracle on whole sequences' rows of one head, sized to about --cpu-seconds
+        threads = oracle.default_threads()
+        sample, pairs, t0 = [], 0, time.perf_counter()
+        seq_pairs = varlen_visible_pairs(wl)
+        budget = args.cpu_seconds
+        for b in range(wl.B):
+            rows_b = [(int(tq), 0) for tq in range(inp.cu_q[b], inp.cu_q[b + 1])]
+            oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows_b, wl.mask, threads)
+            sample.append(b)
+            pairs += int(seq_pairs[b])
+            if time.perf_counter() - t0 > budget:
+                break
+        dt = time.perf_counter() - t0
+        result["cpu_baseline"] = {"value": 4.0 * 128 * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
+                                  "kind": "oracle",
+                                  "sample": f"every query row of head 0 of sequences {sample[0]}..{sample[-1]} of "
+                                            f"{wl.name} ({pairs} visible pairs, fp64 with 3 roundings), {dt:.2f} s"}
     print(json.dumps(result), flush=True)
 
 

@@ -7,10 +7,14 @@ only, every step of the computation runs in the HIP library
     attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
     attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream) -> status
     attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream) -> status
+    attn_fwd_bf16_varlen(q, k, v, o, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q, round_mode, mask,
+                         stream) -> status
     attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
     attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
     attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True, mask="none") -> torch.Tensor
+    attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None, round_mode="rtne",
+                    mask="none") -> torch.Tensor
 """
 from __future__ import annotations
 
@@ -18,7 +22,8 @@ import ctypes
 import os
 
 __all__ = [
-    "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_gqa", "attn_fwd_bf16_ws", "attn_fwd_bf16_workspace_size",
+    "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_gqa", "attn_fwd_bf16_varlen", "attn_fwd_bf16_ws",
+    "attn_fwd_varlen", "attn_fwd_bf16_workspace_size",
     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
     "AttnError", "LAYOUTS", "ROUND_MODES", "MASKS", "library_path", "load_library",
 ]
@@ -64,6 +69,9 @@ def load_library():
         lib.attn_fwd_bf16_gqa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, vp]
         lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
+        lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_int, vp]
+        lib.attn_fwd_bf16_varlen.restype = ctypes.c_int
         lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
                                          vp]
         lib.attn_fwd_bf16_ws.restype = ctypes.c_int
@@ -95,6 +103,13 @@ def attn_fwd_bf16_gqa(q: int, k: int, v: int, o: int, B: int, H: int, H_kv: int,
                       layout: int, round_mode: int, mask: int, stream: int) -> int:
     """The grouped-query C entry point with raw device addresses; returns the status code."""
     return load_library().attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream)
+
+
+def attn_fwd_bf16_varlen(q: int, k: int, v: int, o: int, cu_q: int, cu_k: int, B: int, H: int, H_kv: int,
+                         total_q: int, total_k: int, max_seqlen_q: int, round_mode: int, mask: int, stream: int) -> int:
+    """The variable-length C entry point with raw device addresses; returns the status code."""
+    return load_library().attn_fwd_bf16_varlen(q, k, v, o, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
+                                               round_mode, mask, stream)
 
 
 def attn_fwd_bf16_ws(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int, layout: int,
@@ -195,6 +210,44 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         else:
             status = attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
                                    LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
+    if status != 0:
+        raise AttnError(status)
+    return out
+
+
+def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, out=None, round_mode: str = "rtne",
+                    mask: str = "none", stream=None):
+    """Variable-length batch: ``q`` [total_q, H, 128], ``k``/``v`` [total_k, H_kv, 128]
+    bf16 and ``cu_seqlens_q``/``cu_seqlens_k`` int32 [B+1] offsets, all on one
+    device; sequence b attends within its own rows (attn_fwd_bf16_varlen).
+    ``max_seqlen_q`` must be at least every sequence's query length."""
+    import torch
+
+    if round_mode not in ROUND_MODES or mask not in MASKS:
+        raise ValueError(f"round_mode must be one of {sorted(ROUND_MODES)} and mask one of {sorted(MASKS)}")
+    if q.dim() != 3 or k.dim() != 3 or q.shape[2] != HEAD_DIM or k.shape[2] != HEAD_DIM or v.shape != k.shape:
+        raise ValueError(f"expected q [total_q, H, 128] and k, v [total_k, H_kv, 128], got {tuple(q.shape)}, "
+                         f"{tuple(k.shape)}, {tuple(v.shape)}")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor on q's device")
+    for name, t in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if t.dtype != torch.int32 or t.dim() != 1 or not t.is_contiguous() or t.device != q.device:
+            raise ValueError(f"{name} must be a contiguous int32 vector on q's device")
+    if cu_seqlens_k.numel() != cu_seqlens_q.numel() or cu_seqlens_q.numel() < 2:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 >= 2 offsets")
+    total_q, H, _ = q.shape
+    total_k, H_kv, _ = k.shape
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    with torch.cuda.device(q.device):
+        s = stream if stream is not None else torch.cuda.current_stream(q.device)
+        status = attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
+                                      H, H_kv, total_q, total_k, max_seqlen_q, ROUND_MODES[round_mode], MASKS[mask],
+                                      s.cuda_stream)
     if status != 0:
         raise AttnError(status)
     return out

@@ -138,6 +138,18 @@ struct Split {
   float* ml;
 };
 
+// Variable-length batches: sequence b holds the packed query rows
+// cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1 (offsets read on
+// the device, clamped to [0, total] so that no access leaves the tensors
+// whatever they hold).
+struct Varlen {
+  const int* cu_q;
+  const int* cu_k;
+  int total_q;
+  int total_k;
+  int n_groups;  // B * H_kv: (sequence, K/V head) groups
+};
+
 // Combine a per-lane value with the one held 32 lanes away (the other half of
 // the wave).  This goes through ds_bpermute: AMD clang 22 folds
 // fmaxf(r[0], r[1]) of __builtin_amdgcn_permlane32_swap(x, x) into r[0], as
@@ -199,16 +211,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 
 // SPLIT: the grid may hold split work items (sp describes them); without it
 // every workgroup runs one whole item and the key range is known statically.
+// VARLEN (not with SPLIT): the items are (sequence, head, q-tile) of a packed
+// variable-length batch; Sq and Sk are the sequence's own, and items past a
+// sequence's last q-tile exit at once.
 // CAUSAL (not with SPLIT): query row r attends to the keys
-// j <= min(r + causal_off, Sk - 1) only.  The workgroup visits the key tiles
+// j <= min(r + causal_off, Sk - 1) only, causal_off = 0, or Sk - Sq with
+// causal_br.  The workgroup visits the key tiles
 // 0 .. up to its last row's limit in order (so the q-tiles of a head stream
 // the same tiles together, as without a mask): those every row sees whole in
 // a loop without mask code, then the diagonal ones (some row's limit falls
 // inside or before them) with the mask applied beside the row maxima.
-template <int MODE, bool SPLIT, bool CAUSAL>
+template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, int H, int Sq, int Sk, int n_qtiles, Geometry g, Split sp, int causal_off) {
+    uint16_t* __restrict__ O, int H, int Sq_all, int Sk_all, int n_qtiles, Geometry g, Split sp, Varlen vl,
+    int causal_br) {
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
@@ -219,9 +236,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // Whole items: workgroups are dispatched round-robin over the 8 XCDs;
   // renumber so that XCD x receives a contiguous range of logical work items
   // (a head's q-tiles share one XCD's L2).  Split items follow in id order.
-  const int n_tiles_all = (Sk + BN - 1) / BN;
   const int id = blockIdx.x;
-  int work, t_begin = 0, t_end = n_tiles_all, slot = -1;
+  int work, t_begin = 0, t_end = (Sk_all + BN - 1) / BN, slot = -1;
   if (!SPLIT || id < sp.n_whole) {
     const int xcd = id & 7, local = id >> 3;
     const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
@@ -230,13 +246,27 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     slot = id - sp.n_whole;
     work = sp.n_whole + slot / sp.splits;
     t_begin = (slot % sp.splits) * sp.tiles_per_split;
-    t_end = t_begin + sp.tiles_per_split < n_tiles_all ? t_begin + sp.tiles_per_split : n_tiles_all;
+    t_end = t_begin + sp.tiles_per_split < t_end ? t_begin + sp.tiles_per_split : t_end;
   }
   // causal: a head's q-tiles in decreasing order, the ones with the most
   // visible keys dispatched first
-  const int qt = CAUSAL ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles;
-  const int bh = work / n_qtiles;
-  const int h = bh % H, b = bh / H;
+  int qt = CAUSAL ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles;
+  int h = (work / n_qtiles) % H, b = work / n_qtiles / H;
+  if constexpr (VARLEN) {
+    // Sequences differ in length, so contiguous item ranges per XCD would
+    // load them unevenly.  Instead the (sequence, K/V head) groups are dealt
+    // to the XCDs in turn (with H_kv = 8 every XCD gets one K/V head of every
+    // sequence); a group's items (its query heads x q-tiles, the heads of one
+    // q-tile together) stay on one XCD and share that K/V head in its L2.
+    const int hpg = (int)g.kv_group, gitems = hpg * n_qtiles;
+    const int xcd = id & 7, local = id >> 3;
+    const int group = xcd + 8 * (local / gitems), r = local % gitems;
+    if (group >= vl.n_groups) return;
+    const int H_kv = H / hpg;
+    b = group / H_kv;
+    h = (group % H_kv) * hpg + r % hpg;
+    qt = CAUSAL ? n_qtiles - 1 - r / hpg : r / hpg;
+  }
 
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -244,11 +274,36 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   const int l32 = lane & 31;
   const int grp = lane >> 5;
 
-  const uint16_t* Qh = Q + b * g.q_batch + h * g.q_head;
+  // this item's sequence: its lengths and the element offsets of its first
+  // query and key rows (batch b of the tensors, or packed rows with VARLEN)
+  int Sq = Sq_all, Sk = Sk_all;
+  int64_t q_base = b * g.q_batch, k_base = b * g.k_batch;
+  if constexpr (VARLEN) {
+    const int q0 = min(max(vl.cu_q[b], 0), vl.total_q), q1 = min(max(vl.cu_q[b + 1], q0), vl.total_q);
+    const int k0 = min(max(vl.cu_k[b], 0), vl.total_k), k1 = min(max(vl.cu_k[b + 1], k0), vl.total_k);
+    Sq = q1 - q0;
+    Sk = k1 - k0;
+    q_base = (int64_t)q0 * g.q_row;
+    k_base = (int64_t)k0 * g.k_row;
+    if (qt * BM >= Sq) return;  // past the sequence's last q-tile (the whole workgroup leaves)
+  }
+  const int n_tiles_all = (Sk + BN - 1) / BN;
+  const int causal_off = causal_br ? Sk - Sq : 0;
+  const uint16_t* Qh = Q + q_base + h * g.q_head;
   const int hk = h / (int)g.kv_group;
-  const uint16_t* Kh = K + b * g.k_batch + hk * g.k_head;
-  const uint16_t* Vh = V + b * g.k_batch + hk * g.k_head;
-  uint16_t* Oh = O + b * g.q_batch + h * g.q_head;
+  const uint16_t* Kh = K + k_base + hk * g.k_head;
+  const uint16_t* Vh = V + k_base + hk * g.k_head;
+  uint16_t* Oh = O + q_base + h * g.q_head;
+  if (VARLEN && Sk == 0) {
+    // a sequence without keys: the 0/0 of an empty softmax, NaN rows
+    const int row = qt * BM + (int)(threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
+    if (row < Sq) {
+      uint16_t* dst = Oh + (int64_t)row * g.q_row + 64 * ((threadIdx.x >> 5) & 1);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(u32x4*)(dst + 8 * i) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+    }
+    return;
+  }
   const uint32_t row_bytes = (uint32_t)(g.k_row * 2);
 
   // ---- Q fragments: this lane's query row, dims 16ks + 8grp .. +7 ----
@@ -788,18 +843,26 @@ Geometry make_geometry(int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layo
 
 template <int MODE>
 void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
-            int n_qtiles, const Geometry& g, const Split& sp, int64_t n_wg, int n_split_items, int mask,
-            hipStream_t s) {
-  const int causal_off = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
+            int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg, int n_split_items,
+            int mask, hipStream_t s) {
+  const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
+  const Varlen none{nullptr, nullptr, 0, 0, 0};
+  const dim3 grid((unsigned)n_wg), block(NTHREADS);
   if (n_split_items > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
-                       o, H, Sq, Sk, n_qtiles, g, sp, 0);
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, none, 0);
+  else if (vl && mask != ATTN_MASK_NONE)
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, *vl, br);
+  else if (vl)
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, *vl, 0);
   else if (mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
-                       o, H, Sq, Sk, n_qtiles, g, sp, causal_off);
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, none, br);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false>), dim3((unsigned)n_wg), dim3(NTHREADS), 0, s, q, k, v,
-                       o, H, Sq, Sk, n_qtiles, g, sp, 0);
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, none, 0);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
@@ -808,7 +871,8 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
 }
 
 int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
-        int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream) {
+        int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream,
+        const Varlen* vl = nullptr) {
   const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
   Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
   if (plan.n_split_items > 0) {
@@ -822,16 +886,16 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
   const int nsi = (int)plan.n_split_items;
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
-      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
-                             s);
+      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                             mask, s);
       break;
     case ATTN_ROUND_RTNA:
-      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
-                             s);
+      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                             mask, s);
       break;
     default:
-      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, n_wg, nsi, mask,
-                             s);
+      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                             mask, s);
       break;
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -869,6 +933,50 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
 extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                                     int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* stream) {
   return attn_fwd_bf16_gqa(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, mask, stream);
+}
+
+extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+                                    const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B, int64_t H,
+                                    int64_t H_kv, int64_t total_q, int64_t total_k, int64_t max_seqlen_q,
+                                    int round_mode, int mask, void* stream) {
+  if (!q || !k || !v || !o || !cu_seqlens_q || !cu_seqlens_k) return ATTN_ERR_NULL;
+  if (B < 1 || H < 1 || H_kv < 1 || total_q < 1 || total_k < 1 || max_seqlen_q < 1) return ATTN_ERR_SIZE;
+  if (H % H_kv != 0) return ATTN_ERR_HEADS;
+  Problem pb;
+  int64_t rows_q, rows_k;
+  if (B > INT32_MAX - 1 || total_q > INT32_MAX || total_k > INT32_MAX || max_seqlen_q > INT32_MAX ||
+      H > (1 << 20) || !mul_ok(total_q, H, &rows_q) || !mul_ok(rows_q, 2 * D, &pb.bytes_q) ||
+      !mul_ok(total_k, H_kv, &rows_k) || !mul_ok(rows_k, 2 * D, &pb.bytes_k))
+    return ATTN_ERR_SIZE;
+  pb.n_qtiles = (max_seqlen_q + BM - 1) / BM;
+  pb.n_tiles = 1;
+  int64_t bh;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, pb.n_qtiles, &pb.n_work) || pb.n_work > INT32_MAX - 65536)
+    return ATTN_ERR_SIZE;
+  if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
+    return ATTN_ERR_ROUND;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) ||
+      (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3))
+    return ATTN_ERR_ALIGN;
+  const int64_t cu_bytes = (B + 1) * 4;
+  if (overlaps(o, pb.bytes_q, q, pb.bytes_q) || overlaps(o, pb.bytes_q, k, pb.bytes_k) ||
+      overlaps(o, pb.bytes_q, v, pb.bytes_k) || overlaps(o, pb.bytes_q, cu_seqlens_q, cu_bytes) ||
+      overlaps(o, pb.bytes_q, cu_seqlens_k, cu_bytes))
+    return ATTN_ERR_ALIAS;
+  // grid: 8 XCDs x ceil(groups / 8) groups each x the items of a group
+  const int64_t n_groups = B * H_kv, per_group = (H / H_kv) * pb.n_qtiles;
+  int64_t n_wg;
+  if (!mul_ok(8 * ((n_groups + 7) / 8), per_group, &n_wg) || n_wg > INT32_MAX - 65536) return ATTN_ERR_SIZE;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  const Varlen vl{cu_seqlens_q, cu_seqlens_k, (int)total_q, (int)total_k, (int)n_groups};
+  pb.n_work = n_wg;
+  const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
+  return run(q, k, v, o, H, H_kv, max_seqlen_q, 1, ATTN_LAYOUT_BSHD, round_mode, mask, pb, whole, nullptr, stream,
+             &vl);
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {

@@ -9,7 +9,7 @@
  *
  * without a mask (attn_fwd_bf16_masked adds a causal one), head_dim fixed at
  * 128, one head count shared by Q, K and V (attn_fwd_bf16_gqa allows fewer
- * K/V heads), any
+ * K/V heads; attn_fwd_bf16_varlen takes packed sequences of their own lengths), any
  * query length Sq and key length Sk (cross-attention allowed), inputs read in
  * the BSHD or BHSD layout without a transpose (same page, section "Hvad er
  * udgivet" / What was released).  Output is bf16, rounded per call in one of
@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 4
+#define ATTN_FWD_ABI_VERSION 5
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -186,6 +186,44 @@ int attn_fwd_bf16_masked(const void *q, const void *k, const void *v, void *o,
 int attn_fwd_bf16_gqa(const void *q, const void *k, const void *v, void *o,
                       int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
                       int layout, int round_mode, int mask, void *stream);
+
+/*
+ * attn_fwd_bf16_varlen -- attn_fwd_bf16_gqa over a batch of sequences of
+ * their own lengths, packed one after another (variable-length batching).
+ *
+ * The snilld.dk page lists varlen batching among what the kernel it
+ * describes leaves out and what serving with mixed lengths needs (sections
+ * "Hvad er udgivet" / What was released and "Autoregressiv serving, de
+ * praktiske hager") without defining it; this is the packed layout of
+ * FlashAttention's varlen interface.  Sequence b holds the query rows
+ * cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 of q and o and the key rows
+ * cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of k and v, and attends only within
+ * itself, as its own fixed-length problem (a causal mask is aligned per
+ * sequence; a sequence with queries but no keys gives NaN rows).
+ *
+ *   q, o    : [total_q, H, 128] bf16 (one layout, the rows of all sequences
+ *             in order; row t, head h at (t*H + h)*128).
+ *   k, v    : [total_k, H_kv, 128].
+ *   cu_seqlens_q, cu_seqlens_k : device pointers to B+1 int32 offsets,
+ *             non-decreasing, from 0 to total_q (total_k); 4-byte aligned.
+ *             Read by the kernel; offsets outside [0, total] are clamped to
+ *             it, so no access leaves the tensors whatever they hold (the
+ *             results are then unspecified).
+ *   B       : number of sequences; H, H_kv as attn_fwd_bf16_gqa.
+ *   total_q, total_k : packed row counts (>= 1).
+ *   max_seqlen_q : at least every sequence's query length: the grid covers
+ *             ceil(max_seqlen_q / 256) q-tiles per sequence and head; rows
+ *             of a longer sequence past that are not written.
+ *   round_mode, mask, stream : as attn_fwd_bf16_gqa.
+ *
+ * Status codes as attn_fwd_bf16_gqa (ATTN_ERR_ALIGN also for the offset
+ * arrays, ATTN_ERR_ALIAS also when o overlaps them).  Single pass.
+ */
+int attn_fwd_bf16_varlen(const void *q, const void *k, const void *v, void *o,
+                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                         int64_t B, int64_t H, int64_t H_kv, int64_t total_q,
+                         int64_t total_k, int64_t max_seqlen_q, int round_mode,
+                         int mask, void *stream);
 
 /*
  * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs

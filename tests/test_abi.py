@@ -26,8 +26,8 @@ def _enum_values():
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
     assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_masked",
-                     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_workspace_size",
-                     "attn_fwd_bf16_ws"]
+                     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_varlen",
+                     "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
     exported = set(re.findall(r"\bT\s+(\w+)$", out, re.M))
@@ -118,6 +118,31 @@ def test_gqa_alias_check_uses_the_kv_head_count():
     k_bytes = 1 * 1 * 8 * 256
     assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes, 1, 4, 1, 1, 8, 0, 0, 7, 0) == ev["ATTN_ERR_MASK"]
     assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes - 256, 1, 4, 1, 1, 8, 0, 0, 0, 0) == ev["ATTN_ERR_ALIAS"]
+
+
+CQ, CK = 0x50000, 0x50100  # fake offset arrays (never dereferenced)
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, CQ, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 0, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, CQ, 0, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, CQ, CK, 0, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 0, 10, 8, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 10, 0, 8, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 10, 10, 0, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 1 << 40, 10, 8, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 3, 10, 10, 8, 0, 0), "ATTN_ERR_HEADS"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 10, 10, 8, 3, 0), "ATTN_ERR_ROUND"),
+    ((A, B_, C, O_, CQ, CK, 2, 4, 2, 10, 10, 8, 0, 4), "ATTN_ERR_MASK"),
+    ((A, B_, C, O_, CQ + 2, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A + 8, B_, C, O_, CQ, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, CQ - 64, CQ, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, A + 512, CQ, CK, 2, 4, 2, 10, 10, 8, 0, 0), "ATTN_ERR_ALIAS"),
+])
+def test_varlen_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_varlen(*args, 0) == ev[code]
 
 
 def test_binding_rejects_unknown_mask_name():

@@ -150,3 +150,39 @@ def test_causal_bottom_right_prefill_odd_lengths():
 def test_grouped_query_causal_8k():
     # B=2 H=32 H_kv=8 Sq=Sk=8192 BSHD RTNE, causal: query head h uses K/V head h / 4
     _run_config("gqa8k_causal")
+
+
+@pytest.mark.timeout(600)
+def test_varlen_mix_causal():
+    # 16 packed causal sequences of 732 .. 7793 tokens (77048 in all), H=32 over H_kv=8, RTNE:
+    # seeded rows plus the first and last rows of every sequence, checked one by one
+    from tests.gpu_util import to_bits, to_device
+
+    wl = synth.VARLEN_WORKLOADS["varlen_mix"]
+    inp = synth.generate_varlen(wl)
+    total_q = inp.q.shape[0]
+    flat = synth.floyd_sample(wl.seed, synth.TID_SUBSET, total_q * wl.H, 768, stream=4242)
+    rows = {(f // wl.H, f % wl.H) for f in flat}
+    for b in range(wl.B):
+        for t in (inp.cu_q[b], inp.cu_q[b] + 255, inp.cu_q[b] + 256, inp.cu_q[b + 1] - 1):
+            if inp.cu_q[b] <= t < inp.cu_q[b + 1]:
+                rows.add((int(t), (3 * b) % wl.H))
+    rows = sorted(rows)
+    ex, rd = oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows, wl.mask)
+    q, k, v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+    cq, ck = torch.from_numpy(inp.cu_q).to("cuda:0"), torch.from_numpy(inp.cu_k).to("cuda:0")
+    o = torch.empty_like(q)
+    outs = []
+    for _ in range(2):
+        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+                                       ck.data_ptr(), wl.B, wl.H, wl.H_kv, total_q, inp.k.shape[0],
+                                       max(wl.lengths_q), attn.ROUND_MODES["rtne"], attn.MASKS[wl.mask],
+                                       torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        torch.cuda.synchronize()
+        outs.append(to_bits(o))
+    assert np.array_equal(outs[0], outs[1]), "repeated launch changed the output"
+    got = np.stack([outs[0][t, h] for t, h in rows])
+    res = gate(got, rd[:, 0], ex)
+    say(f"  varlen_mix rtne: {res.summary()}")
+    assert res.ok, res.summary()
