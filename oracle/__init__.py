@@ -96,7 +96,7 @@ def _load():
                                                 i64p, i64, f64p, u16p, ctypes.c_int]
         lib.oracle_attn_rows_masked.restype = ctypes.c_int
         lib.oracle_attn_rows_gqa.argtypes = [u16p, u16p, u16p, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
-                                             i64p, i64, f64p, u16p, ctypes.c_int]
+                                             i64p, i64, f64p, u16p, f64p, ctypes.c_int]
         lib.oracle_attn_rows_gqa.restype = ctypes.c_int
         lib.oracle_softmax_row.argtypes = [u16p, u16p, i64, i64, i64, i64, ctypes.c_int,
                                            i64, i64, i64, f64p]
@@ -147,7 +147,7 @@ def _check_inputs(q, k, v, B, H, H_kv, Sq, Sk, layout):
 
 
 def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nthreads: int | None = None,
-              mask: str = "none"):
+              mask: str = "none", with_lse: bool = False):
     """Exact outputs of the given (b, h, i) query rows and their roundings.
 
     ``q``/``k``/``v`` are bf16 bit arrays stored in ``layout`` (k and v may
@@ -155,7 +155,8 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
     ``MASKS``.  Returns
     ``(o_exact, o_round)``: ``o_exact`` is float64 [n, 128] and ``o_round``
     uint16 [n, 3, 128] in the mode order RTNE, RTNA, RTZ; both follow the
-    order of ``rows``.
+    order of ``rows``.  With ``with_lse`` a third array holds each row's
+    log-sum-exp (float64 [n]; see attn_oracle.c for its special values).
     """
     if layout == "bshd":
         B, Sq, H, _ = q.shape
@@ -170,15 +171,18 @@ def attn_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, layout: str, rows, nt
     srt = np.ascontiguousarray(rows[order])
     o_exact = np.empty((n, D), dtype=np.float64)
     o_round = np.empty((n, 3, D), dtype=np.uint16)
+    lse = np.empty(n, dtype=np.float64)
     if mask not in MASKS:
         raise ValueError(f"mask must be one of {sorted(MASKS)}, got {mask!r}")
     rc = _load().oracle_attn_rows_gqa(_u16(q), _u16(k), _u16(v), B, H, H_kv, Sq, Sk, LAYOUTS[layout], MASKS[mask],
                                       srt.ctypes.data_as(ctypes.POINTER(ctypes.c_int64)), n,
-                                      _f64(o_exact), _u16(o_round), nthreads or default_threads())
+                                      _f64(o_exact), _u16(o_round), _f64(lse), nthreads or default_threads())
     if rc != 0:
         raise RuntimeError(f"oracle_attn_rows failed with {rc}")
     inv = np.empty_like(order)
     inv[order] = np.arange(n)
+    if with_lse:
+        return o_exact[inv], o_round[inv], lse[inv]
     return o_exact[inv], o_round[inv]
 
 
@@ -210,7 +214,7 @@ def softmax_row(q, k, layout: str, b: int, h: int, i: int):
 
 
 def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, rows, mask: str = "none",
-                     nthreads: int | None = None):
+                     nthreads: int | None = None, with_lse: bool = False):
     """Exact outputs of packed query rows of a variable-length batch.
 
     ``q`` is [total_q, H, 128] and ``k``/``v`` [total_k, H_kv, 128] bf16 bits:
@@ -221,7 +225,8 @@ def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, ro
     key rows in BSHD, handed to ``attn_rows`` as such; a sequence with no key
     gives NaN rows (the 0/0 of an empty softmax).  ``rows`` are (t, h) pairs
     of packed query row and head.  Returns ``(o_exact, o_round)`` like
-    ``attn_rows``.
+    ``attn_rows`` (and the log-sum-exp of each row with ``with_lse``: -Inf for
+    a sequence without keys).
     """
     cu_q = np.asarray(cu_q, dtype=np.int64)
     cu_k = np.asarray(cu_k, dtype=np.int64)
@@ -234,6 +239,7 @@ def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, ro
     n = rows.shape[0]
     o_exact = np.full((n, D), np.nan)
     o_round = np.full((n, 3, D), 0x7FC0, dtype=np.uint16)
+    lse = np.full(n, -np.inf)
     seq = np.searchsorted(cu_q, rows[:, 0], side="right") - 1
     for b in np.unique(seq):
         sel = np.nonzero(seq == b)[0]
@@ -241,10 +247,13 @@ def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, ro
         if k1 == k0:
             continue  # no key: NaN rows
         sub = [(0, int(h), int(t - q0)) for t, h in rows[sel]]
-        ex, rd = attn_rows(np.ascontiguousarray(q[q0:q1][None]), np.ascontiguousarray(k[k0:k1][None]),
-                           np.ascontiguousarray(v[k0:k1][None]), "bshd", sub, nthreads, mask)
+        ex, rd, ls = attn_rows(np.ascontiguousarray(q[q0:q1][None]), np.ascontiguousarray(k[k0:k1][None]),
+                               np.ascontiguousarray(v[k0:k1][None]), "bshd", sub, nthreads, mask, with_lse=True)
         o_exact[sel] = ex
         o_round[sel] = rd
+        lse[sel] = ls
+    if with_lse:
+        return o_exact, o_round, lse
     return o_exact, o_round
 
 

@@ -48,6 +48,14 @@
  * multiple of H_kv, and query head h attends with K/V head h / (H / H_kv)
  * (consecutive query heads share one K/V head).  Everything else is as above.
  *
+ * Log-sum-exp.  Per query row, lse = log(sum_j exp(s_j)) over the keys the
+ * row sees (natural log, the logits of step 2), the per-row statistic the
+ * FlashAttention family keeps for a backward pass or for merging key ranges;
+ * the pages do not discuss it (an extension the survey lists after GQA and
+ * varlen).  Evaluated as m + log(l) from steps 3-4 when m is finite; -Inf
+ * when the row sees no key or only -Inf logits (the log of an empty or zero
+ * sum); NaN when m is NaN or +Inf (the rows whose output is NaN as well).
+ *
  * Pins (tests/test_oracle_*.py): closed forms, invariants, brute force on
  * tiny inputs, a library softmax cross-check and exhaustive/definitional
  * checks of the rounding and decoding.
@@ -180,10 +188,12 @@ static int64_t visible_keys(int mask, int64_t i, int64_t Sq, int64_t Sk)
 }
 
 /* Steps 2-4 for one query row against the first Sk keys of a decoded head.
- * On return w[j] holds exp(s_j - m) and the function returns
- * l = sum_j w_j (0 when there are no keys). */
-static double row_weights(const double *qrow, const double *Kd, int64_t Sk, double *w)
+ * On return w[j] holds exp(s_j - m), *m_out the maximum m (-Inf when there
+ * are no keys), and the function returns l = sum_j w_j (0 when there are no
+ * keys). */
+static double row_weights(const double *qrow, const double *Kd, int64_t Sk, double *w, double *m_out)
 {
+    *m_out = -INFINITY;
     if (Sk == 0)
         return 0.0;
     const double sqrt_d = sqrt((double)D);
@@ -202,7 +212,18 @@ static double row_weights(const double *qrow, const double *Kd, int64_t Sk, doub
         w[j] = exp(w[j] - m);
         l += w[j];
     }
+    *m_out = m;
     return l;
+}
+
+/* The log-sum-exp of a row from its maximum and shifted sum (see the header). */
+static double row_lse(double m, double l)
+{
+    if (isfinite(m))
+        return m + log(l);
+    if (m == -INFINITY)
+        return -INFINITY;
+    return NAN;
 }
 
 /* Step 5 for one row. */
@@ -231,6 +252,7 @@ typedef struct {
     int64_t lo, hi;      /* row range within rows */
     double *o_exact;     /* nrows x D */
     uint16_t *o_round;   /* nrows x 3 x D */
+    double *lse;         /* nrows, or NULL */
     int ok;
 } job_t;
 
@@ -248,9 +270,12 @@ static void *run_job(void *arg)
         for (int c = 0; c < D; ++c)
             qrow[c] = oracle_bf16_decode(jb->q[offset_of(jb->layout, jb->H, jb->Sq, jb->b, jb->h, i, c)]);
         const int64_t n = visible_keys(jb->mask, i, jb->Sq, jb->Sk);
-        double l = row_weights(qrow, jb->Kd, n, w);
+        double m;
+        double l = row_weights(qrow, jb->Kd, n, w, &m);
         double *o = jb->o_exact + r * D;
         row_output(w, l, jb->Vd, n, o);
+        if (jb->lse)
+            jb->lse[r] = row_lse(m, l);
         for (int mode = 0; mode < 3; ++mode)
             for (int c = 0; c < D; ++c)
                 jb->o_round[(r * 3 + mode) * D + c] = oracle_round_bf16(o[c], mode);
@@ -275,6 +300,7 @@ static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int
  *   with Sk rows and H_kv heads (H a multiple of H_kv).
  *   mask: OR_MASK_NONE, OR_MASK_CAUSAL_TOP_LEFT or OR_MASK_CAUSAL_BOTTOM_RIGHT.
  *   rows: nrows triples (b, h, i); rows with equal (b, h) must be adjacent.
+ *   lse: nrows binary64 log-sum-exp values, or NULL.
  *   o_exact: nrows x 128 binary64;  o_round: nrows x 3 x 128 bf16 bits
  *   (modes in the order RTNE, RTNA, RTZ).
  *   nthreads: worker threads (rows of one head are split among them).
@@ -283,7 +309,7 @@ static void decode_head(const uint16_t *t, int layout, int64_t H, int64_t S, int
 int oracle_attn_rows_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v,
                          int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int mask,
                          const int64_t *rows, int64_t nrows,
-                         double *o_exact, uint16_t *o_round, int nthreads)
+                         double *o_exact, uint16_t *o_round, double *lse, int nthreads)
 {
     if (!q || !k || !v || !rows || !o_exact || !o_round)
         return -1;
@@ -324,7 +350,7 @@ int oracle_attn_rows_gqa(const uint16_t *q, const uint16_t *k, const uint16_t *v
             jb->q = q, jb->H = H, jb->Sq = Sq, jb->b = b, jb->h = h, jb->layout = layout;
             jb->Kd = Kd, jb->Vd = Vd, jb->Sk = Sk, jb->mask = mask, jb->rows = rows;
             jb->lo = r0 + n * t / nt, jb->hi = r0 + n * (t + 1) / nt;
-            jb->o_exact = o_exact, jb->o_round = o_round, jb->ok = 0;
+            jb->o_exact = o_exact, jb->o_round = o_round, jb->lse = lse, jb->ok = 0;
         }
         int started = 0;
         for (int t = 1; t < nt; ++t) {
@@ -352,7 +378,8 @@ int oracle_attn_rows_masked(const uint16_t *q, const uint16_t *k, const uint16_t
                             const int64_t *rows, int64_t nrows,
                             double *o_exact, uint16_t *o_round, int nthreads)
 {
-    return oracle_attn_rows_gqa(q, k, v, B, H, H, Sq, Sk, layout, mask, rows, nrows, o_exact, o_round, nthreads);
+    return oracle_attn_rows_gqa(q, k, v, B, H, H, Sq, Sk, layout, mask, rows, nrows, o_exact, o_round, NULL,
+                                nthreads);
 }
 
 /* oracle_attn_rows: the unmasked case of oracle_attn_rows_masked. */
@@ -381,7 +408,8 @@ double oracle_softmax_row(const uint16_t *q, const uint16_t *k,
     double qrow[D];
     for (int c = 0; c < D; ++c)
         qrow[c] = oracle_bf16_decode(q[offset_of(layout, H, Sq, b, h, i, c)]);
-    double l = row_weights(qrow, Kd, Sk, w);
+    double m;
+    double l = row_weights(qrow, Kd, Sk, w, &m);
     for (int64_t j = 0; j < Sk; ++j)
         w[j] /= l;
     free(Kd);

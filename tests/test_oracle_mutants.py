@@ -36,6 +36,10 @@ MUTANTS = {
     "causal_alignments_swapped": ("OR_MASK_CAUSAL_TOP_LEFT ? 0 : Sk - Sq;", "OR_MASK_CAUSAL_TOP_LEFT ? Sk - Sq : 0;"),
     "causal_empty_row_zero": ("    if (Sk == 0)\n        return 0.0;", "    if (Sk == 0)\n        return 1.0;"),
     "gqa_k_head_modulo": ("decode_head(k, layout, H_kv, Sk, b, h / group, Kd);", "decode_head(k, layout, H_kv, Sk, b, h % H_kv, Kd);"),
+    "lse_drops_the_max": ("        return m + log(l);", "        return log(l);"),
+    "lse_base_two": ("        return m + log(l);", "        return m + log2(l);"),
+    "lse_empty_row_nan": ("    if (m == -INFINITY)\n        return -INFINITY;\n    return NAN;",
+                          "    if (m == -INFINITY)\n        return NAN;\n    return NAN;"),
     "gqa_v_head_modulo": ("decode_head(v, layout, H_kv, Sk, b, h / group, Vd);", "decode_head(v, layout, H_kv, Sk, b, h % H_kv, Vd);"),
 }
 
@@ -53,7 +57,7 @@ def test_mutant_is_caught(name, tmp_path):
     env = dict(os.environ, ORACLE_LIB=str(lib))
     r = subprocess.run([sys.executable, "-m", "pytest", "-x", "-q", "-p", "no:cacheprovider",
                         "tests/test_oracle_attention.py", "tests/test_oracle_causal.py",
-                        "tests/test_oracle_gqa.py", "tests/test_oracle_rounding.py"],
+                        "tests/test_oracle_gqa.py", "tests/test_oracle_lse.py", "tests/test_oracle_rounding.py"],
                        cwd=ROOT, env=env, capture_output=True, text=True, timeout=600)
     assert r.returncode != 0, f"mutant {name} passed every pin:\n{r.stdout[-2000:]}"
 
