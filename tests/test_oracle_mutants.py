@@ -68,8 +68,8 @@ def test_mutant_is_caught(name, tmp_path):
 # against it.
 PY_SRC = os.path.join(ROOT, "oracle", "__init__.py")
 PY_MUTANTS = {
-    "varlen_keys_shifted": ("np.ascontiguousarray(k[k0:k1][None]),\n                           np.ascontiguousarray(v[k0:k1][None])",
-                            "np.ascontiguousarray(k[k0 + 1:k1 + 1][None]),\n                           np.ascontiguousarray(v[k0 + 1:k1 + 1][None])"),
+    "varlen_keys_shifted": ("np.ascontiguousarray(k[k0:k1][None]),\n                               np.ascontiguousarray(v[k0:k1][None])",
+                            "np.ascontiguousarray(k[k0 + 1:k1 + 1][None]),\n                               np.ascontiguousarray(v[k0 + 1:k1 + 1][None])"),
     "varlen_queries_of_next_sequence": ("q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]",
                                         "q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[min(b + 1, B - 1)], cu_k[min(b + 2, B)]"),
     "varlen_empty_keys_zero": ("o_exact = np.full((n, D), np.nan)", "o_exact = np.zeros((n, D))"),
