@@ -222,7 +222,7 @@ def main():
         if ws_bytes > 0:
             st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
         elif grouped:
-            st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], wl.B, wl.H, wl.kv_heads, wl.Sq,
+            st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads, wl.Sq,
                                         wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], stream.cuda_stream)
         elif masked:
             st = attn.attn_fwd_bf16_masked(*args_c, attn.MASKS[wl.mask], stream.cuda_stream)
@@ -338,7 +338,7 @@ def main_varlen(args):
     log(f"[bench] entry point: {entry}")
 
     def step():
-        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, cq.data_ptr(),
                                        ck.data_ptr(), wl.B, wl.H, wl.H_kv, q.shape[0], k.shape[0], max_q,
                                        attn.ROUND_MODES[mode], attn.MASKS[wl.mask], stream.cuda_stream)
         if st != 0:

@@ -6,9 +6,9 @@ only, every step of the computation runs in the HIP library
 
     attn_fwd_bf16(q, k, v, o, B, H, Sq, Sk, layout, round_mode, stream) -> status
     attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream) -> status
-    attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream) -> status
-    attn_fwd_bf16_varlen(q, k, v, o, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q, round_mode, mask,
-                         stream) -> status
+    attn_fwd_bf16_gqa(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream) -> status
+    attn_fwd_bf16_varlen(q, k, v, o, lse, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q, round_mode,
+                         mask, stream) -> status
     attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
     attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
@@ -66,10 +66,10 @@ def load_library():
         lib.attn_fwd_bf16_masked.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, vp]
         lib.attn_fwd_bf16_masked.restype = ctypes.c_int
-        lib.attn_fwd_bf16_gqa.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+        lib.attn_fwd_bf16_gqa.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                           ctypes.c_int, vp]
         lib.attn_fwd_bf16_gqa.restype = ctypes.c_int
-        lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+        lib.attn_fwd_bf16_varlen.argtypes = [vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, ctypes.c_int,
                                              ctypes.c_int, vp]
         lib.attn_fwd_bf16_varlen.restype = ctypes.c_int
         lib.attn_fwd_bf16_ws.argtypes = [vp, vp, vp, vp, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp, i64,
@@ -99,17 +99,21 @@ def attn_fwd_bf16_masked(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int
     return load_library().attn_fwd_bf16_masked(q, k, v, o, B, H, Sq, Sk, layout, round_mode, mask, stream)
 
 
-def attn_fwd_bf16_gqa(q: int, k: int, v: int, o: int, B: int, H: int, H_kv: int, Sq: int, Sk: int,
+def attn_fwd_bf16_gqa(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, Sq: int, Sk: int,
                       layout: int, round_mode: int, mask: int, stream: int) -> int:
-    """The grouped-query C entry point with raw device addresses; returns the status code."""
-    return load_library().attn_fwd_bf16_gqa(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream)
+    """The grouped-query C entry point with raw device addresses (lse 0: not
+    written); returns the status code."""
+    return load_library().attn_fwd_bf16_gqa(q, k, v, o, lse or None, B, H, H_kv, Sq, Sk, layout, round_mode, mask,
+                                            stream)
 
 
-def attn_fwd_bf16_varlen(q: int, k: int, v: int, o: int, cu_q: int, cu_k: int, B: int, H: int, H_kv: int,
-                         total_q: int, total_k: int, max_seqlen_q: int, round_mode: int, mask: int, stream: int) -> int:
-    """The variable-length C entry point with raw device addresses; returns the status code."""
-    return load_library().attn_fwd_bf16_varlen(q, k, v, o, cu_q, cu_k, B, H, H_kv, total_q, total_k, max_seqlen_q,
-                                               round_mode, mask, stream)
+def attn_fwd_bf16_varlen(q: int, k: int, v: int, o: int, lse: int, cu_q: int, cu_k: int, B: int, H: int,
+                         H_kv: int, total_q: int, total_k: int, max_seqlen_q: int, round_mode: int, mask: int,
+                         stream: int) -> int:
+    """The variable-length C entry point with raw device addresses (lse 0: not
+    written); returns the status code."""
+    return load_library().attn_fwd_bf16_varlen(q, k, v, o, lse or None, cu_q, cu_k, B, H, H_kv, total_q, total_k,
+                                               max_seqlen_q, round_mode, mask, stream)
 
 
 def attn_fwd_bf16_ws(q: int, k: int, v: int, o: int, B: int, H: int, Sq: int, Sk: int, layout: int,
@@ -160,7 +164,7 @@ def _dims(q, k, layout: str):
 
 
 def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None,
-             split: bool = True, mask: str = "none"):
+             split: bool = True, mask: str = "none", with_lse: bool = False):
     """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
 
     ``q`` [B,Sq,H,128] and ``k``/``v`` [B,Sk,H_kv,128] for "bshd", or
@@ -171,7 +175,9 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
     ``split`` the key range may be split (attn_fwd_bf16_ws, workspace from
     torch); without, the single-pass attn_fwd_bf16.  ``mask`` "causal" or
     "causal_br" (attn_fwd_bf16_masked) lets row i see keys j <= i or
-    j <= i + Sk - Sq only; masked calls run single-pass.
+    j <= i + Sk - Sq only; masked calls run single-pass.  ``with_lse``
+    returns ``(out, lse)`` with lse [B, H, Sq] fp32, each row's log-sum-exp
+    (through attn_fwd_bf16_gqa, single pass).
     """
     import torch
 
@@ -194,10 +200,13 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
-        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and mask == "none" and H_kv == H else 0
-        if H_kv != H:
-            status = attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, H_kv, Sq,
-                                       Sk, LAYOUTS[layout], ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
+        lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if with_lse else None
+        direct = mask == "none" and H_kv == H and not with_lse
+        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and direct else 0
+        if H_kv != H or with_lse:
+            status = attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr() if with_lse else 0, B, H, H_kv, Sq, Sk, LAYOUTS[layout],
+                                       ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
         elif mask != "none":
             status = attn_fwd_bf16_masked(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
                                           LAYOUTS[layout], ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)
@@ -212,15 +221,16 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
                                    LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
     if status != 0:
         raise AttnError(status)
-    return out
+    return (out, lse) if with_lse else out
 
 
 def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, out=None, round_mode: str = "rtne",
-                    mask: str = "none", stream=None):
+                    mask: str = "none", stream=None, with_lse: bool = False):
     """Variable-length batch: ``q`` [total_q, H, 128], ``k``/``v`` [total_k, H_kv, 128]
     bf16 and ``cu_seqlens_q``/``cu_seqlens_k`` int32 [B+1] offsets, all on one
     device; sequence b attends within its own rows (attn_fwd_bf16_varlen).
-    ``max_seqlen_q`` must be at least every sequence's query length."""
+    ``max_seqlen_q`` must be at least every sequence's query length.
+    ``with_lse`` returns ``(out, lse)`` with lse [H, total_q] fp32."""
     import torch
 
     if round_mode not in ROUND_MODES or mask not in MASKS:
@@ -242,12 +252,14 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, out=
         out = torch.empty_like(q)
     elif out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
         raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if with_lse else None
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         status = attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                      lse.data_ptr() if with_lse else 0,
                                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
                                       H, H_kv, total_q, total_k, max_seqlen_q, ROUND_MODES[round_mode], MASKS[mask],
                                       s.cuda_stream)
     if status != 0:
         raise AttnError(status)
-    return out
+    return (out, lse) if with_lse else out

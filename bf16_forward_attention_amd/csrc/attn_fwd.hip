@@ -225,7 +225,7 @@ template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq_all, int Sk_all, int n_qtiles, Geometry g, Split sp, Varlen vl,
-    int causal_br) {
+    int causal_br, float* __restrict__ lse) {
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
@@ -278,6 +278,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // query and key rows (batch b of the tensors, or packed rows with VARLEN)
   int Sq = Sq_all, Sk = Sk_all;
   int64_t q_base = b * g.q_batch, k_base = b * g.k_batch;
+  // log-sum-exp of query row i of this item: lse[lse_row0 + i], laid out
+  // [B, H, Sq] (VARLEN: [H, total_q])
+  int64_t lse_row0 = ((int64_t)b * H + h) * Sq_all;
   if constexpr (VARLEN) {
     const int q0 = min(max(vl.cu_q[b], 0), vl.total_q), q1 = min(max(vl.cu_q[b + 1], q0), vl.total_q);
     const int k0 = min(max(vl.cu_k[b], 0), vl.total_k), k1 = min(max(vl.cu_k[b + 1], k0), vl.total_k);
@@ -285,6 +288,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     Sk = k1 - k0;
     q_base = (int64_t)q0 * g.q_row;
     k_base = (int64_t)k0 * g.k_row;
+    lse_row0 = (int64_t)h * vl.total_q + q0;
     if (qt * BM >= Sq) return;  // past the sequence's last q-tile (the whole workgroup leaves)
   }
   const int n_tiles_all = (Sk + BN - 1) / BN;
@@ -295,12 +299,15 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   const uint16_t* Vh = V + k_base + hk * g.k_head;
   uint16_t* Oh = O + q_base + h * g.q_head;
   if (VARLEN && Sk == 0) {
-    // a sequence without keys: the 0/0 of an empty softmax, NaN rows
+    // a sequence without keys: the 0/0 of an empty softmax, NaN rows; the
+    // log of an empty sum, -Inf
     const int row = qt * BM + (int)(threadIdx.x >> 6) * 32 + (threadIdx.x & 31);
     if (row < Sq) {
-      uint16_t* dst = Oh + (int64_t)row * g.q_row + 64 * ((threadIdx.x >> 5) & 1);
+      const int half = (threadIdx.x >> 5) & 1;
+      uint16_t* dst = Oh + (int64_t)row * g.q_row + 64 * half;
 #pragma unroll
       for (int i = 0; i < 8; ++i) *(u32x4*)(dst + 8 * i) = u32x4{0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u};
+      if (lse && half == 0) lse[lse_row0 + row] = -__builtin_inff();
     }
     return;
   }
@@ -671,6 +678,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     if (grp == 0) *(f32x2*)(sp.ml + ((int64_t)slot * BM + row) * 2) = f32x2{m_run, l_tot};
     return;
   }
+  // the row's log-sum-exp: the logits of this kernel are t = s log2(e)/sqrt(128),
+  // sum_j 2^t_j = 2^m l, so ln(sum_j exp(s_j / sqrt(128))) = ln(2) (m + log2 l)
+  // (l = 0: -Inf; l NaN: NaN)
+  if (lse && grp == 0 && qrow < Sq) lse[lse_row0 + qrow] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
   // normalise, round, store this lane's query row
   const float inv_l = 1.0f / l_tot;
   if (qrow < Sq) {
@@ -844,25 +855,25 @@ Geometry make_geometry(int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layo
 template <int MODE>
 void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
             int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg, int n_split_items,
-            int mask, hipStream_t s) {
+            int mask, float* lse, hipStream_t s) {
   const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
   const Varlen none{nullptr, nullptr, 0, 0, 0};
   const dim3 grid((unsigned)n_wg), block(NTHREADS);
   if (n_split_items > 0)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0);
+                       n_qtiles, g, sp, none, 0, nullptr);
   else if (vl && mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, br);
+                       n_qtiles, g, sp, *vl, br, lse);
   else if (vl)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, 0);
+                       n_qtiles, g, sp, *vl, 0, lse);
   else if (mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, br);
+                       n_qtiles, g, sp, none, br, lse);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0);
+                       n_qtiles, g, sp, none, 0, lse);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
@@ -872,7 +883,7 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
 
 int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
         int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream,
-        const Varlen* vl = nullptr) {
+        const Varlen* vl = nullptr, float* lse = nullptr) {
   const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
   Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
   if (plan.n_split_items > 0) {
@@ -887,15 +898,15 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
       launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, s);
+                             mask, lse, s);
       break;
     case ATTN_ROUND_RTNA:
       launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, s);
+                             mask, lse, s);
       break;
     default:
       launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, s);
+                             mask, lse, s);
       break;
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -915,27 +926,35 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
   return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream);
 }
 
-extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
-                                 int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode, int mask,
-                                 void* stream) {
+extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                 int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode,
+                                 int mask, void* stream) {
   Problem pb;
   const int st = check_args(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
+  if (lse) {
+    // [B, H, Sq] fp32; B*H*Sq*256 is the (checked) size of q, so this fits
+    const int64_t lse_bytes = pb.bytes_q / 64;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    if (overlaps(lse, lse_bytes, q, pb.bytes_q) || overlaps(lse, lse_bytes, k, pb.bytes_k) ||
+        overlaps(lse, lse_bytes, v, pb.bytes_k) || overlaps(lse, lse_bytes, o, pb.bytes_q))
+      return ATTN_ERR_ALIAS;
+  }
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_MASK;
   int n_cu = 0;
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream);
+  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream, nullptr, lse);
 }
 
 extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
                                     int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* stream) {
-  return attn_fwd_bf16_gqa(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, mask, stream);
+  return attn_fwd_bf16_gqa(q, k, v, o, nullptr, B, H, H, Sq, Sk, layout, round_mode, mask, stream);
 }
 
-extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o,
+extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int64_t B, int64_t H,
                                     int64_t H_kv, int64_t total_q, int64_t total_k, int64_t max_seqlen_q,
                                     int round_mode, int mask, void* stream) {
@@ -955,8 +974,6 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
     return ATTN_ERR_SIZE;
   if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
     return ATTN_ERR_ROUND;
-  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
-    return ATTN_ERR_MASK;
   if ((((uintptr_t)q | (uintptr_t)k | (uintptr_t)v | (uintptr_t)o) & 15) ||
       (((uintptr_t)cu_seqlens_q | (uintptr_t)cu_seqlens_k) & 3))
     return ATTN_ERR_ALIGN;
@@ -965,6 +982,17 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
       overlaps(o, pb.bytes_q, v, pb.bytes_k) || overlaps(o, pb.bytes_q, cu_seqlens_q, cu_bytes) ||
       overlaps(o, pb.bytes_q, cu_seqlens_k, cu_bytes))
     return ATTN_ERR_ALIAS;
+  if (lse) {
+    // [H, total_q] fp32
+    const int64_t lse_bytes = pb.bytes_q / 64;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    if (overlaps(lse, lse_bytes, q, pb.bytes_q) || overlaps(lse, lse_bytes, k, pb.bytes_k) ||
+        overlaps(lse, lse_bytes, v, pb.bytes_k) || overlaps(lse, lse_bytes, o, pb.bytes_q) ||
+        overlaps(lse, lse_bytes, cu_seqlens_q, cu_bytes) || overlaps(lse, lse_bytes, cu_seqlens_k, cu_bytes))
+      return ATTN_ERR_ALIAS;
+  }
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
   // grid: 8 XCDs x ceil(groups / 8) groups each x the items of a group
   const int64_t n_groups = B * H_kv, per_group = (H / H_kv) * pb.n_qtiles;
   int64_t n_wg;
@@ -976,7 +1004,7 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
   pb.n_work = n_wg;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
   return run(q, k, v, o, H, H_kv, max_seqlen_q, 1, ATTN_LAYOUT_BSHD, round_mode, mask, pb, whole, nullptr, stream,
-             &vl);
+             &vl, lse);
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {

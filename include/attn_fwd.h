@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 5
+#define ATTN_FWD_ABI_VERSION 6
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -175,17 +175,27 @@ int attn_fwd_bf16_masked(const void *q, const void *k, const void *v, void *o,
  * attention; H_kv = H: attn_fwd_bf16_masked).
  *
  *   q, o    : [B, Sq, H, 128] (BSHD) or [B, H, Sq, 128] (BHSD).
+ *   lse     : NULL, or device memory for B*H*Sq fp32 values laid out
+ *             [B, H, Sq] (either layout), 4-byte aligned, not overlapping
+ *             q, k, v or o: receives each query row's log-sum-exp
+ *             ln(sum_j exp(q.k_j / sqrt(128))) over the keys the row sees,
+ *             the per-row statistic a backward pass or a merge of key
+ *             ranges needs (the FlashAttention family's softmax_lse); -Inf
+ *             for a row that sees no key or only -Inf logits, NaN where the
+ *             output row is NaN.  Computed in fp32 from the row's running
+ *             maximum and sum.
  *   k, v    : [B, Sk, H_kv, 128] (BSHD) or [B, H_kv, Sk, 128] (BHSD).
  *   H_kv    : K/V head count, >= 1, dividing H.
  *   mask    : attn_mask_t, as attn_fwd_bf16_masked.
  *   other arguments : as attn_fwd_bf16.
  *
  * Status codes as attn_fwd_bf16_masked, plus ATTN_ERR_HEADS (H not a
- * multiple of H_kv; H_kv < 1 is ATTN_ERR_SIZE).
+ * multiple of H_kv; H_kv < 1 is ATTN_ERR_SIZE) and ATTN_ERR_ALIGN /
+ * ATTN_ERR_ALIAS for lse.
  */
 int attn_fwd_bf16_gqa(const void *q, const void *k, const void *v, void *o,
-                      int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
-                      int layout, int round_mode, int mask, void *stream);
+                      float *lse, int64_t B, int64_t H, int64_t H_kv, int64_t Sq,
+                      int64_t Sk, int layout, int round_mode, int mask, void *stream);
 
 /*
  * attn_fwd_bf16_varlen -- attn_fwd_bf16_gqa over a batch of sequences of
@@ -203,6 +213,9 @@ int attn_fwd_bf16_gqa(const void *q, const void *k, const void *v, void *o,
  *
  *   q, o    : [total_q, H, 128] bf16 (one layout, the rows of all sequences
  *             in order; row t, head h at (t*H + h)*128).
+ *   lse     : NULL, or H*total_q fp32 laid out [H, total_q] (packed row
+ *             index), as attn_fwd_bf16_gqa's (-Inf for a sequence without
+ *             keys).
  *   k, v    : [total_k, H_kv, 128].
  *   cu_seqlens_q, cu_seqlens_k : device pointers to B+1 int32 offsets,
  *             non-decreasing, from 0 to total_q (total_k); 4-byte aligned.
@@ -217,10 +230,10 @@ int attn_fwd_bf16_gqa(const void *q, const void *k, const void *v, void *o,
  *   round_mode, mask, stream : as attn_fwd_bf16_gqa.
  *
  * Status codes as attn_fwd_bf16_gqa (ATTN_ERR_ALIGN also for the offset
- * arrays, ATTN_ERR_ALIAS also when o overlaps them).  Single pass.
+ * arrays, ATTN_ERR_ALIAS also when o or lse overlaps them).  Single pass.
  */
 int attn_fwd_bf16_varlen(const void *q, const void *k, const void *v, void *o,
-                         const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                         float *lse, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                          int64_t B, int64_t H, int64_t H_kv, int64_t total_q,
                          int64_t total_k, int64_t max_seqlen_q, int round_mode,
                          int mask, void *stream);

@@ -78,3 +78,34 @@ def gate(gpu_bits: np.ndarray, oracle_bits: np.ndarray, oracle_exact: np.ndarray
     rms = float(np.sqrt(np.mean(np.where(fin, (g - ex) ** 2, 0.0))) / scale) if scale > 0 else 0.0
     return GateResult(viol == 0 and nan_mis == 0 and inf_mis == 0, int(fin.sum()), viol, nan_mis, inf_mis,
                       float(dist.max()) if dist.size else 0.0, hist, rms)
+
+
+def lse_tolerance(dot_abs_max: np.ndarray, n_keys: np.ndarray, lse_ref: np.ndarray) -> np.ndarray:
+    """Per-row bound on |lse_gpu - lse_exact| for the fp32 kernel.
+
+    lse = ln 2 (m + log2 l) from fp32 logits and an fp32 running sum:
+      * each logit is an fp32 sum of 128 exact products: |ds| <= 128 u sum_c |q_c k_c|
+        (u = 2^-24), and lse moves by at most the largest logit error
+        (dot_abs_max = max_j sum_c |q_c k_jc| / sqrt(128));
+      * the scaled exponent fma(s, c, -m) and exp2 add a few ulp per weight;
+      * the row sum of n weights in fp32, 32 per tile then tile by tile, is off
+        by at most (32 + n/64) u relatively (plus one rounding per rescale),
+        which moves the log by as much;
+      * log2, the add of m and the product by ln 2 round the result: a few ulp of |lse|.
+    The bound is twice the sum of these terms.
+    """
+    u = 2.0**-24
+    d = 128 * u * dot_abs_max + 4 * u * dot_abs_max + (32 + n_keys / 64 + 64) * u + 8 * u * (1 + np.abs(lse_ref))
+    return 2 * d
+
+
+def lse_gate(got: np.ndarray, ref: np.ndarray, tol: np.ndarray):
+    """(ok, worst |err|/tol, count) for fp32 lse against the oracle's binary64:
+    NaN and +-Inf at the same positions, finite values within ``tol``."""
+    got = np.asarray(got, dtype=np.float64)
+    same_special = np.array_equal(np.isnan(got), np.isnan(ref)) and np.array_equal(np.isposinf(got), np.isposinf(ref)) \
+        and np.array_equal(np.isneginf(got), np.isneginf(ref))
+    fin = np.isfinite(ref) & np.isfinite(got)
+    ratio = np.abs(got[fin] - ref[fin]) / tol[fin] if fin.any() else np.zeros(0)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    return same_special and worst <= 1.0, worst, int(fin.sum())

@@ -59,7 +59,7 @@ def launch_masked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Te
 
 
 def launch_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
-               mask: str = "none", stream: torch.cuda.Stream | None = None) -> None:
+               mask: str = "none", stream: torch.cuda.Stream | None = None, lse: torch.Tensor | None = None) -> None:
     """Call attn_fwd_bf16_gqa through the C ABI; the K/V head count comes from k's shape."""
     if layout == "bshd":
         B, Sq, H, _ = q.shape
@@ -68,7 +68,8 @@ def launch_gqa(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tenso
         B, H, Sq, _ = q.shape
         H_kv, Sk = k.shape[1], k.shape[2]
     s = stream if stream is not None else torch.cuda.current_stream()
-    st = attn.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), B, H, H_kv, Sq, Sk,
+    st = attn.attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                lse.data_ptr() if lse is not None else 0, B, H, H_kv, Sq, Sk,
                                 attn.LAYOUTS[layout], attn.ROUND_MODES[mode], attn.MASKS[mask], s.cuda_stream)
     if st != 0:
         raise attn.AttnError(st)

@@ -109,15 +109,15 @@ def test_masked_argument_errors_before_any_hip_call(args, code):
 ])
 def test_gqa_argument_errors_before_any_hip_call(args, code):
     ev = _enum_values()
-    assert attn.attn_fwd_bf16_gqa(*args, 0) == ev[code]
+    assert attn.attn_fwd_bf16_gqa(*args[:4], 0, *args[4:], 0) == ev[code]
 
 
 def test_gqa_alias_check_uses_the_kv_head_count():
     # k holds B*H_kv*Sk rows of 256 B: with H_kv = 1, o placed right after k does not overlap it
     ev = _enum_values()
     k_bytes = 1 * 1 * 8 * 256
-    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes, 1, 4, 1, 1, 8, 0, 0, 7, 0) == ev["ATTN_ERR_MASK"]
-    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes - 256, 1, 4, 1, 1, 8, 0, 0, 0, 0) == ev["ATTN_ERR_ALIAS"]
+    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes, 0, 1, 4, 1, 1, 8, 0, 0, 7, 0) == ev["ATTN_ERR_MASK"]
+    assert attn.attn_fwd_bf16_gqa(A, B_, C, B_ + k_bytes - 256, 0, 1, 4, 1, 1, 8, 0, 0, 0, 0) == ev["ATTN_ERR_ALIAS"]
 
 
 CQ, CK = 0x50000, 0x50100  # fake offset arrays (never dereferenced)
@@ -142,7 +142,22 @@ CQ, CK = 0x50000, 0x50100  # fake offset arrays (never dereferenced)
 ])
 def test_varlen_argument_errors_before_any_hip_call(args, code):
     ev = _enum_values()
-    assert attn.attn_fwd_bf16_varlen(*args, 0) == ev[code]
+    assert attn.attn_fwd_bf16_varlen(*args[:4], 0, *args[4:], 0) == ev[code]
+
+
+L_ = 0x60000  # a fake lse array
+
+
+@pytest.mark.parametrize("lse,code", [
+    (L_ + 2, "ATTN_ERR_ALIGN"),   # not 4-byte aligned
+    (A + 256, "ATTN_ERR_ALIAS"),  # inside q
+    (O_ + 64, "ATTN_ERR_ALIAS"),  # inside o
+    (O_ + 4 * 2 * 256, "ATTN_ERR_MASK"),  # just past o (4 heads x 2 rows x 256 B): fine, then the bad mask
+])
+def test_lse_argument_errors(lse, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_gqa(A, B_, C, O_, lse, 1, 4, 2, 2, 8, 0, 0, 9, 0) == ev[code]
+    assert attn.attn_fwd_bf16_varlen(A, B_, C, O_, lse, CQ, CK, 1, 4, 2, 2, 8, 2, 0, 9, 0) == ev[code]
 
 
 def test_binding_rejects_unknown_mask_name():

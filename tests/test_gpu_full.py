@@ -174,7 +174,7 @@ def test_varlen_mix_causal():
     o = torch.empty_like(q)
     outs = []
     for _ in range(2):
-        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+        st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, cq.data_ptr(),
                                        ck.data_ptr(), wl.B, wl.H, wl.H_kv, total_q, inp.k.shape[0],
                                        max(wl.lengths_q), attn.ROUND_MODES["rtne"], attn.MASKS[wl.mask],
                                        torch.cuda.current_stream().cuda_stream)

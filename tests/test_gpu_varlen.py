@@ -42,7 +42,7 @@ def _run(inp, mode, mask, max_q=None):
     cq = torch.from_numpy(inp.cu_q).to("cuda:0")
     ck = torch.from_numpy(inp.cu_k).to("cuda:0")
     o = torch.full_like(q, float("nan"))
-    st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+    st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, cq.data_ptr(),
                                    ck.data_ptr(), wl.B, wl.H, wl.H_kv, q.shape[0], k.shape[0],
                                    max_q or max(max(wl.lengths_q), 1), attn.ROUND_MODES[mode], attn.MASKS[mask],
                                    torch.cuda.current_stream().cuda_stream)
@@ -96,7 +96,7 @@ def test_offsets_outside_the_tensors_are_clamped():
     o = o_all[: q.shape[0]]
     cq = torch.tensor([0, 40, 1000], dtype=torch.int32, device="cuda:0")
     ck = torch.tensor([0, 50, -7], dtype=torch.int32, device="cuda:0")
-    st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), cq.data_ptr(),
+    st = attn.attn_fwd_bf16_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), 0, cq.data_ptr(),
                                    ck.data_ptr(), 2, 2, 2, q.shape[0], k.shape[0], 1000, 0, 0,
                                    torch.cuda.current_stream().cuda_stream)
     assert st == 0
