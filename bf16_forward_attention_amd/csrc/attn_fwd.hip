@@ -1,5 +1,7 @@
-// attn_fwd.hip -- fused bf16 forward attention for MI355X (gfx950), without a
-// mask or with a causal one.
+// attn_fwd.hip -- fused bf16 forward attention for MI355X (gfx950): without a
+// mask or with a causal one, with as many K/V heads as query heads or fewer,
+// over fixed-length or packed variable-length batches, with an optional
+// per-row log-sum-exp.
 //
 // O = softmax(Q K^T / sqrt(128)) V per (batch, head, query row), the
 // operation the snilld.dk page "Open source attention kernel in HIP beats
@@ -25,6 +27,14 @@
 // sum, and attn_merge_kernel combines them (the same max-shifted sums as the
 // online softmax) before the one rounding to bf16.
 //
+// Extensions the pages list as missing from the kernel they describe (their
+// section "Hvad er udgivet" / What was released): a causal mask (CAUSAL: the
+// tiles past a row's limit are never visited, the diagonal ones are masked
+// beside the row maxima), grouped K/V heads (query head h reads K/V head
+// h / kv_group) and packed variable-length batches (VARLEN: each sequence's
+// offsets read on the device).  The per-row log-sum-exp comes from the same
+// running maximum and sum as the output.
+//
 // MFMA 32x32x16 operand layout (lane l, g = l / 32):
 //     A[i][k]: lane supplies row i = l % 32, k = 8g .. 8g+7
 //     B[k][j]: lane supplies column j = l % 32, k = 8g .. 8g+7
@@ -47,8 +57,8 @@
 // logits of tile t into weights (exp2, row sum, bf16 pack), then the P.V
 // product of tile t while the VALU reduces the row maxima of tile t+1.  The
 // loads of tile t+3 are issued one instruction at a time between MFMAs.
-// When Sk is not a multiple of 64 the ragged last key tile is visited first,
-// so the one key mask happens before the loop.
+// Without a causal mask, when Sk is not a multiple of 64 the ragged last key
+// tile is visited first, so the one key mask happens before the loop.
 //
 // Key order inside a 32-key block.  LDS K row i holds key
 // pi(i) = 16*(i/4 % 2) + 4*(i/8) + i%4, so that after the first product lane
