@@ -96,6 +96,11 @@ namespace {
 constexpr int D = 128;
 constexpr int BM = 256;                // query rows per workgroup
 constexpr int BN = 64;                 // keys per tile
+// The tile loads address the 64 K/V rows of a tile with 32-bit buffer
+// offsets: 63 row strides + 256 bytes must stay below 2^32.  The row stride is
+// H_kv * 256 bytes in BSHD and packed layouts, so H_kv (and H >= H_kv) is
+// capped at 2^18: 63 * 2^26 + 256 < 2^32.
+constexpr int64_t kMaxHeads = int64_t(1) << 18;
 constexpr int NWAVES = BM / 32;        // 32 query rows per wave: 8 waves, two per SIMD
 constexpr int NTHREADS = NWAVES * 64;
 constexpr int TILE_BYTES = BN * D * 2; // one K or V tile in LDS (16 KiB)
@@ -827,9 +832,8 @@ int check_args(const void* q, const void* k, const void* v, const void* o, int64
     return ATTN_ERR_SIZE;
   pb->n_qtiles = (Sq + BM - 1) / BM;
   pb->n_tiles = (Sk + BN - 1) / BN;
-  // one 64-key tile of rows must be addressable by 32-bit buffer offsets
   if (!mul_ok(bh, pb->n_qtiles, &pb->n_work) || pb->n_work > INT32_MAX - 65536 || Sq > INT32_MAX ||
-      Sk > INT32_MAX || H > (1 << 20))
+      Sk > INT32_MAX || H > kMaxHeads)
     return ATTN_ERR_SIZE;
   if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
   if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
@@ -974,7 +978,7 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
   Problem pb;
   int64_t rows_q, rows_k;
   if (B > INT32_MAX - 1 || total_q > INT32_MAX || total_k > INT32_MAX || max_seqlen_q > INT32_MAX ||
-      H > (1 << 20) || !mul_ok(total_q, H, &rows_q) || !mul_ok(rows_q, 2 * D, &pb.bytes_q) ||
+      H > kMaxHeads || !mul_ok(total_q, H, &rows_q) || !mul_ok(rows_q, 2 * D, &pb.bytes_q) ||
       !mul_ok(total_k, H_kv, &rows_k) || !mul_ok(rows_k, 2 * D, &pb.bytes_k))
     return ATTN_ERR_SIZE;
   pb.n_qtiles = (max_seqlen_q + BM - 1) / BM;

@@ -69,7 +69,7 @@ typedef enum {
 typedef enum {
     ATTN_OK = 0,
     ATTN_ERR_NULL = 1,   /* a tensor pointer is NULL */
-    ATTN_ERR_SIZE = 2,   /* B, H, Sq or Sk < 1, or a byte size overflows int64 */
+    ATTN_ERR_SIZE = 2,   /* B, H, Sq or Sk < 1, H > 2^18, or a size overflows the index types */
     ATTN_ERR_LAYOUT = 3, /* layout is not an attn_layout_t value */
     ATTN_ERR_ROUND = 4,  /* round_mode is not an attn_round_t value */
     ATTN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned */

@@ -67,6 +67,8 @@ A, B_, C, O_ = 0x10000, 0x20000, 0x30000, 0x40000  # distinct aligned fake addre
     ((A, B_, C, O_, 1, 1, 1, 0, 0, 0), "ATTN_ERR_SIZE"),
     ((A, B_, C, O_, 1, -3, 1, 1, 0, 0), "ATTN_ERR_SIZE"),
     ((A, B_, C, O_, 1 << 40, 1 << 20, 1, 1, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 1, (1 << 18) + 1, 1, 1, 0, 0), "ATTN_ERR_SIZE"),  # 64 K rows past 32-bit offsets
+    ((A, B_, C, O_, 1, 1 << 18, 1, 1, 0, 5), "ATTN_ERR_ROUND"),       # the largest head count passes the size checks
     ((A, B_, C, O_, 1, 1, 1, 1, 2, 0), "ATTN_ERR_LAYOUT"),
     ((A, B_, C, O_, 1, 1, 1, 1, -1, 0), "ATTN_ERR_LAYOUT"),
     ((A, B_, C, O_, 1, 1, 1, 1, 0, 3), "ATTN_ERR_ROUND"),
