@@ -4,8 +4,9 @@
 A step is one call of the library over the whole workload (every query row of
 every head), inputs resident in HBM: attn_fwd_bf16_ws with a preallocated
 workspace when the shape splits its key ranges (then the step is both of its
-kernels), attn_fwd_bf16_gqa for the grouped-query workloads,
-attn_fwd_bf16_masked for the causal ones, attn_fwd_bf16 otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
+kernels; attn_fwd_bf16_gqa_ws for the causal and grouped-query workloads),
+attn_fwd_bf16_gqa for grouped-query or causal workloads that do not split,
+attn_fwd_bf16 otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
 BSHD, RTNE.  Prints one JSON line:
 
   value      forward TFLOP/s, 4*128 FLOPs per visible (query, key) pair (all
@@ -51,7 +52,7 @@ def parse():
     p.add_argument("--workload", default="self8k")
     p.add_argument("--mode", default=None, help="rounding mode (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--no-split", action="store_true", help="always call attn_fwd_bf16 (single pass)")
+    p.add_argument("--no-split", action="store_true", help="always run single-pass (no key-range split)")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for the sample")
     p.add_argument("--parity-rows", type=int, default=256)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -200,14 +201,24 @@ def main():
     stream = torch.cuda.current_stream(dev)
     masked = wl.mask != "none"
     grouped = wl.kv_heads != wl.H
-    ws_bytes = (0 if args.no_split or masked or grouped
-                else attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk))
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    if args.no_split:
+        ws_bytes = 0
+    elif masked or grouped:
+        ws_bytes = attn.attn_fwd_bf16_gqa_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk, attn.MASKS[wl.mask])
+    else:
+        ws_bytes = attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
     args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
               attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
-    if ws_bytes > 0:
-        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan(
-            wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64), torch.cuda.get_device_properties(dev).multi_processor_count)
+    if ws_bytes > 0 and (masked or grouped):
+        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan_masked(wl.B * wl.H, wl.Sq, wl.Sk,
+                                                                         attn.MASKS[wl.mask], n_cu)
+        entry = (f"attn_fwd_bf16_gqa_ws(H_kv={wl.kv_heads}, {wl.mask}): {whole} work items whole, {items} split "
+                 f"into {splits} key ranges (of up to {tps} tiles), {ws_bytes} B workspace")
+    elif ws_bytes > 0:
+        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan(wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64),
+                                                                  n_cu)
         entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
                  f"{tps} tiles, {ws_bytes} B workspace")
     elif grouped:
@@ -219,7 +230,11 @@ def main():
     log(f"[bench] entry point: {entry}")
 
     def step():
-        if ws_bytes > 0:
+        if ws_bytes > 0 and (masked or grouped):
+            st = attn.attn_fwd_bf16_gqa_ws(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads,
+                                           wl.Sq, wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], ws.data_ptr(),
+                                           ws_bytes, stream.cuda_stream)
+        elif ws_bytes > 0:
             st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
         elif grouped:
             st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads, wl.Sq,

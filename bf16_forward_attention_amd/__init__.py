@@ -11,7 +11,11 @@ only, every step of the computation runs in the HIP library
                          mask, stream) -> status
     attn_fwd_bf16_ws(q, k, v, o, B, H, Sq, Sk, layout, round_mode, ws, ws_bytes, stream) -> status
     attn_fwd_bf16_workspace_size(B, H, Sq, Sk) -> bytes
+    attn_fwd_bf16_gqa_ws(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, ws, ws_bytes,
+                         stream) -> status
+    attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, mask) -> bytes
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
+    attn_fwd_bf16_split_plan_masked(n_heads, Sq, Sk, mask, n_cu) -> the same four numbers
     attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True, mask="none") -> torch.Tensor
     attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, out=None, round_mode="rtne",
                     mask="none") -> torch.Tensor
@@ -23,8 +27,8 @@ import os
 
 __all__ = [
     "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_gqa", "attn_fwd_bf16_varlen", "attn_fwd_bf16_ws",
-    "attn_fwd_varlen", "attn_fwd_bf16_workspace_size",
-    "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
+    "attn_fwd_varlen", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_gqa_workspace_size",
+    "attn_fwd_bf16_split_plan", "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
     "AttnError", "LAYOUTS", "ROUND_MODES", "MASKS", "library_path", "load_library",
 ]
 
@@ -79,6 +83,13 @@ def load_library():
         lib.attn_fwd_bf16_workspace_size.restype = ctypes.c_int
         lib.attn_fwd_bf16_split_plan.argtypes = [i64, i64, i64, ctypes.POINTER(i64)]
         lib.attn_fwd_bf16_split_plan.restype = ctypes.c_int
+        lib.attn_fwd_bf16_gqa_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_int, vp, i64, vp]
+        lib.attn_fwd_bf16_gqa_ws.restype = ctypes.c_int
+        lib.attn_fwd_bf16_gqa_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.POINTER(i64)]
+        lib.attn_fwd_bf16_gqa_workspace_size.restype = ctypes.c_int
+        lib.attn_fwd_bf16_split_plan_masked.argtypes = [i64, i64, i64, ctypes.c_int, i64, ctypes.POINTER(i64)]
+        lib.attn_fwd_bf16_split_plan_masked.restype = ctypes.c_int
         lib.attn_fwd_bf16_strerror.argtypes = [ctypes.c_int]
         lib.attn_fwd_bf16_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_bf16_abi_version.argtypes = []
@@ -132,6 +143,34 @@ def attn_fwd_bf16_workspace_size(B: int, H: int, Sq: int, Sk: int) -> int:
     return out.value
 
 
+def attn_fwd_bf16_gqa_ws(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, Sq: int, Sk: int,
+                         layout: int, round_mode: int, mask: int, workspace: int, workspace_bytes: int,
+                         stream: int) -> int:
+    """The grouped-query, masked C entry point allowed to split the key range
+    (lse 0: not written); returns the status code."""
+    return load_library().attn_fwd_bf16_gqa_ws(q, k, v, o, lse or None, B, H, H_kv, Sq, Sk, layout, round_mode,
+                                               mask, workspace or None, workspace_bytes, stream)
+
+
+def attn_fwd_bf16_gqa_workspace_size(B: int, H: int, Sq: int, Sk: int, mask: int) -> int:
+    """Workspace bytes attn_fwd_bf16_gqa_ws needs on the current device (raises AttnError)."""
+    out = ctypes.c_int64(0)
+    status = load_library().attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, mask, ctypes.byref(out))
+    if status != 0:
+        raise AttnError(status)
+    return out.value
+
+
+def attn_fwd_bf16_split_plan_masked(n_heads: int, Sq: int, Sk: int, mask: int, n_cu: int):
+    """attn_fwd_bf16_gqa_ws's split decision: (items run whole, items split,
+    ranges per split item, tiles per range of the heaviest item)."""
+    out = (ctypes.c_int64 * 4)()
+    status = load_library().attn_fwd_bf16_split_plan_masked(n_heads, Sq, Sk, mask, n_cu, out)
+    if status != 0:
+        raise AttnError(status)
+    return tuple(out)
+
+
 def attn_fwd_bf16_split_plan(n_work: int, n_tiles: int, n_cu: int):
     """(items run whole, items split, ranges per split item, tiles per range)."""
     out = (ctypes.c_int64 * 4)()
@@ -173,11 +212,10 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
     attn_fwd_bf16_gqa.  Enqueued on
     ``stream`` (default: torch's current stream on that device).  With
     ``split`` the key range may be split (attn_fwd_bf16_ws, workspace from
-    torch); without, the single-pass attn_fwd_bf16.  ``mask`` "causal" or
-    "causal_br" (attn_fwd_bf16_masked) lets row i see keys j <= i or
-    j <= i + Sk - Sq only; masked calls run single-pass.  ``with_lse``
-    returns ``(out, lse)`` with lse [B, H, Sq] fp32, each row's log-sum-exp
-    (through attn_fwd_bf16_gqa, single pass).
+    torch; attn_fwd_bf16_gqa_ws with a mask, grouped heads or lse); without,
+    the single-pass entry points.  ``mask`` "causal" or "causal_br" lets row
+    i see keys j <= i or j <= i + Sk - Sq only.  ``with_lse`` returns
+    ``(out, lse)`` with lse [B, H, Sq] fp32, each row's log-sum-exp.
     """
     import torch
 
@@ -202,8 +240,18 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
         lse = torch.empty((B, H, Sq), dtype=torch.float32, device=q.device) if with_lse else None
         direct = mask == "none" and H_kv == H and not with_lse
-        ws_bytes = attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if split and direct else 0
-        if H_kv != H or with_lse:
+        ws_bytes = 0
+        if split:
+            ws_bytes = (attn_fwd_bf16_workspace_size(B, H, Sq, Sk) if direct
+                        else attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, MASKS[mask]))
+        if ws_bytes > 0 and not direct:
+            ws = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+            status = attn_fwd_bf16_gqa_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                          lse.data_ptr() if with_lse else 0, B, H, H_kv, Sq, Sk, LAYOUTS[layout],
+                                          ROUND_MODES[round_mode], MASKS[mask], ws.data_ptr(), ws_bytes,
+                                          s.cuda_stream)
+            ws.record_stream(s)
+        elif H_kv != H or with_lse:
             status = attn_fwd_bf16_gqa(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                        lse.data_ptr() if with_lse else 0, B, H, H_kv, Sq, Sk, LAYOUTS[layout],
                                        ROUND_MODES[round_mode], MASKS[mask], s.cuda_stream)

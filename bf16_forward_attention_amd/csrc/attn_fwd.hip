@@ -229,13 +229,15 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // VARLEN (not with SPLIT): the items are (sequence, head, q-tile) of a packed
 // variable-length batch; Sq and Sk are the sequence's own, and items past a
 // sequence's last q-tile exit at once.
-// CAUSAL (not with SPLIT): query row r attends to the keys
+// CAUSAL: query row r attends to the keys
 // j <= min(r + causal_off, Sk - 1) only, causal_off = 0, or Sk - Sq with
 // causal_br.  The workgroup visits the key tiles
 // 0 .. up to its last row's limit in order (so the q-tiles of a head stream
 // the same tiles together, as without a mask): those every row sees whole in
 // a loop without mask code, then the diagonal ones (some row's limit falls
-// inside or before them) with the mask applied beside the row maxima.
+// inside or before them) with the mask applied beside the row maxima.  With
+// SPLIT, a split item's visible tiles are cut into sp.splits ranges of equal
+// length (the last ones may be shorter or empty).
 template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
@@ -419,6 +421,24 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const int64_t r0 = (int64_t)qt * BM + causal_off;
     const int64_t lo = r0 < last_key ? r0 : last_key;
     diag0 = lo < 0 ? 0 : (int)((lo + 1) / BN);
+    if (SPLIT && slot >= 0) {
+      // this workgroup's share of the item's visible tiles
+      const int per = (n_tiles + sp.splits - 1) / sp.splits;
+      t_begin = (slot % sp.splits) * per;
+      t_end = t_begin + per < n_tiles ? t_begin + per : n_tiles;
+      n_tiles = t_end - t_begin;
+      if (n_tiles <= 0) {
+        // an empty range: the partial of no keys (m = -FLT_MAX, l = 0, rows
+        // 0), which the merge weighs with 0 (or, when no range saw a key,
+        // turns into the 0 * (1/0) = NaN of a row without keys)
+        const int row = wave * 32 + l32;
+        float* prow = sp.part + ((int64_t)slot * BM + row) * D + 4 * grp;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) *(f32x4*)(prow + 8 * i) = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+        if (grp == 0) *(f32x2*)(sp.ml + ((int64_t)slot * BM + row) * 2) = f32x2{-3.402823466e38f, 0.0f};
+        return;
+      }
+    }
   }
   // Buffer resources of the K and V rows of the seq-th visited tile.  Past
   // the last tile the range is empty: those loads touch no memory (the
@@ -612,7 +632,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     asm volatile("" : "+s"(lw));
     qk_weights(S[1 - P], S[P], k_st[(ST + 1) % NSTAGE],
                [&](int u) __attribute__((always_inline)) { dma_k(rk, lw, (ST + 3) % NSTAGE, u); });
-    pv_rowmax(masked_c, ST, S[1 - P], t + 1,
+    pv_rowmax(masked_c, ST, S[1 - P], t_begin + t + 1,
               [&](int u) __attribute__((always_inline)) { dma_v(rv, lw, (ST + 3) % NSTAGE, u); });
   };
   using Plain = std::false_type;
@@ -631,7 +651,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   __syncthreads();
   qk(S[0], k_st[0]);
   if (CAUSAL) {
-    if (diag0 == 0) mask_causal(S[0], 0);
+    if (t_begin >= diag0) mask_causal(S[0], t_begin);
   } else if (ragged && (!SPLIT || t_begin == 0)) {
     mask_tail(S[0], n_tiles_all - 1);
   }
@@ -644,7 +664,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     // iterations (whole rounds of the four stages, their next tiles all
     // before diag0) need no mask; the rest mask whatever tile comes next (a
     // mask on a tile every row sees whole changes nothing).
-    const int n_plain = diag0 > 0 ? ((diag0 - 1) & ~3) : 0;
+    const int n_plain = diag0 > t_begin ? min((diag0 - t_begin - 1) & ~3, n_tiles & ~3) : 0;
     int t = 0;
     while (t < n_plain) {
       body(S0{}, Plain{}, t);
@@ -720,16 +740,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 // (item, row, 4 dims).  A split whose logits were all -Inf has m_s = -FLT_MAX
 // and contributes nothing; a row with no finite logit at all gives 0 * Inf =
 // NaN, as in the whole-row kernel.
+// reverse_qt: the items of each head are in decreasing q-tile order (the
+// causal kernels' order).  With lse, thread 0 of each row also stores the
+// row's log-sum-exp, ln(2) (M + log2 L) with L the merged row sum.
 template <int MODE>
 __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ O, int H, int Sq, int n_qtiles,
-                                                         Geometry g, Split sp, int n_split_items) {
+                                                         Geometry g, Split sp, int n_split_items, int reverse_qt,
+                                                         float* __restrict__ lse) {
   const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (gid >= (int64_t)n_split_items * BM * (D / 4)) return;
   const int c4 = (int)(gid % (D / 4));
   const int row = (int)((gid / (D / 4)) % BM);
   const int item = (int)(gid / ((D / 4) * BM));
   const int work = sp.n_whole + item;
-  const int qt = work % n_qtiles, bh = work / n_qtiles;
+  const int qt = reverse_qt ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles, bh = work / n_qtiles;
   const int h = bh % H, b = bh / H;
   const int qrow = qt * BM + row;
   if (qrow >= Sq) return;
@@ -745,6 +769,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
     num += w * o;
     den += w * ml[1];
   }
+  if (lse && c4 == 0) lse[((int64_t)b * H + h) * Sq + qrow] = (mmax + log2f(den)) * 0.6931471805599453f;
   const float inv = 1.0f / den;
   uint16_t* dst = O + b * g.q_batch + h * g.q_head + (int64_t)qrow * g.q_row + 4 * c4;
   const uint32_t lo = round_to_bf16<MODE>(num[0] * inv) | ((uint32_t)round_to_bf16<MODE>(num[1] * inv) << 16);
@@ -813,6 +838,27 @@ Plan make_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu) {
   p.tiles_per_split = tps;
   return p;
 }
+// Key tiles the q-tile qt visits under a causal mask (row i sees keys
+// j <= i + off, off = 0 or Sk - Sq): up to its last row's limit, and one
+// (fully masked) tile when no row sees a key.
+int64_t causal_tiles(int64_t qt, int64_t Sq, int64_t Sk, int mask) {
+  const int64_t off = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT ? Sk - Sq : 0;
+  const int64_t r_last = (qt * BM + BM < Sq ? qt * BM + BM : Sq) - 1;
+  const int64_t hi = r_last + off < Sk - 1 ? r_last + off : Sk - 1;
+  return hi < 0 ? 1 : hi / BN + 1;
+}
+// Split plan under a mask.  The items of a causal launch differ in length;
+// the last round is split only when they are nearly equal (the lightest
+// q-tile visits at least 3/4 of the tiles of the heaviest, as when Sq is
+// small against Sk with the bottom-right diagonal): otherwise the
+// longest-first item order already keeps the CUs busy to the end.  A split
+// item cuts its own visible tiles into `splits` ranges.
+Plan make_plan_masked(int64_t n_work, int64_t n_qtiles, int64_t Sq, int64_t Sk, int mask, int64_t n_cu) {
+  if (mask == ATTN_MASK_NONE) return make_plan(n_work, (Sk + BN - 1) / BN, n_cu);
+  const int64_t n_max = causal_tiles(n_qtiles - 1, Sq, Sk, mask), n_min = causal_tiles(0, Sq, Sk, mask);
+  if (4 * n_min < 3 * n_max) return Plan{n_work, 0, 1, n_max};
+  return make_plan(n_work, n_max, n_cu);
+}
 int64_t plan_workspace_bytes(const Plan& p) {
   return p.n_split_items * p.splits * BM * (D + 2) * (int64_t)sizeof(float);
 }
@@ -873,9 +919,12 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
   const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
   const Varlen none{nullptr, nullptr, 0, 0, 0};
   const dim3 grid((unsigned)n_wg), block(NTHREADS);
-  if (n_split_items > 0)
+  if (n_split_items > 0 && mask != ATTN_MASK_NONE)
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, sp, none, br, lse);
+  else if (n_split_items > 0)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, nullptr);
+                       n_qtiles, g, sp, none, 0, lse);
   else if (vl && mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, *vl, br, lse);
@@ -891,7 +940,7 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
-                       Sq, n_qtiles, g, sp, n_split_items);
+                       Sq, n_qtiles, g, sp, n_split_items, mask != ATTN_MASK_NONE ? 1 : 0, lse);
   }
 }
 
@@ -1032,6 +1081,23 @@ extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t
   return ATTN_OK;
 }
 
+extern "C" int attn_fwd_bf16_split_plan_masked(int64_t n_heads, int64_t Sq, int64_t Sk, int mask, int64_t n_cu,
+                                               int64_t* out4) {
+  if (!out4) return ATTN_ERR_NULL;
+  int64_t n_work;
+  if (n_heads < 1 || Sq < 1 || Sk < 1 || n_cu < 1 || Sq > INT32_MAX || Sk > INT32_MAX ||
+      !mul_ok(n_heads, (Sq + BM - 1) / BM, &n_work))
+    return ATTN_ERR_SIZE;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  const Plan p = make_plan_masked(n_work, (Sq + BM - 1) / BM, Sq, Sk, mask, n_cu);
+  out4[0] = p.n_whole;
+  out4[1] = p.n_split_items;
+  out4[2] = p.splits;
+  out4[3] = p.tiles_per_split;
+  return ATTN_OK;
+}
+
 extern "C" int attn_fwd_bf16_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int64_t* bytes) {
   if (!bytes) return ATTN_ERR_NULL;
   *bytes = 0;
@@ -1045,6 +1111,58 @@ extern "C" int attn_fwd_bf16_workspace_size(int64_t B, int64_t H, int64_t Sq, in
   if (dev_status != ATTN_OK) return dev_status;
   *bytes = plan_workspace_bytes(make_plan(n_work, (Sk + BN - 1) / BN, n_cu));
   return ATTN_OK;
+}
+
+extern "C" int attn_fwd_bf16_gqa_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk, int mask,
+                                                int64_t* bytes) {
+  if (!bytes) return ATTN_ERR_NULL;
+  *bytes = 0;
+  if (B < 1 || H < 1 || Sq < 1 || Sk < 1) return ATTN_ERR_SIZE;
+  int64_t bh, n_work;
+  const int64_t n_qtiles = (Sq + BM - 1) / BM;
+  if (!mul_ok(B, H, &bh) || !mul_ok(bh, n_qtiles, &n_work) || n_work > INT32_MAX - 65536 || Sq > INT32_MAX ||
+      Sk > INT32_MAX)
+    return ATTN_ERR_SIZE;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  *bytes = plan_workspace_bytes(make_plan_masked(n_work, n_qtiles, Sq, Sk, mask, n_cu));
+  return ATTN_OK;
+}
+
+extern "C" int attn_fwd_bf16_gqa_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                    int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode,
+                                    int mask, void* workspace, int64_t workspace_bytes, void* stream) {
+  Problem pb;
+  const int st = check_args(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, &pb);
+  if (st != ATTN_OK) return st;
+  if (lse) {
+    const int64_t lse_bytes = pb.bytes_q / 64;
+    if ((uintptr_t)lse & 3) return ATTN_ERR_ALIGN;
+    if (overlaps(lse, lse_bytes, q, pb.bytes_q) || overlaps(lse, lse_bytes, k, pb.bytes_k) ||
+        overlaps(lse, lse_bytes, v, pb.bytes_k) || overlaps(lse, lse_bytes, o, pb.bytes_q))
+      return ATTN_ERR_ALIAS;
+  }
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  if (workspace_bytes < 0) return ATTN_ERR_SIZE;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  const Plan plan = make_plan_masked(pb.n_work, pb.n_qtiles, Sq, Sk, mask, n_cu);
+  const int64_t need = plan_workspace_bytes(plan);
+  if (need > 0) {
+    if (!workspace) return ATTN_ERR_NULL;
+    if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
+    if ((uintptr_t)workspace & 15) return ATTN_ERR_ALIGN;
+    if (overlaps(workspace, need, q, pb.bytes_q) || overlaps(workspace, need, k, pb.bytes_k) ||
+        overlaps(workspace, need, v, pb.bytes_k) || overlaps(workspace, need, o, pb.bytes_q) ||
+        (lse && overlaps(workspace, need, lse, pb.bytes_q / 64)))
+      return ATTN_ERR_ALIAS;
+  }
+  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, plan, workspace, stream, nullptr, lse);
 }
 
 extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,

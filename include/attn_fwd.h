@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 6
+#define ATTN_FWD_ABI_VERSION 7
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -237,6 +237,57 @@ int attn_fwd_bf16_varlen(const void *q, const void *k, const void *v, void *o,
                          int64_t B, int64_t H, int64_t H_kv, int64_t total_q,
                          int64_t total_k, int64_t max_seqlen_q, int round_mode,
                          int mask, void *stream);
+
+/*
+ * attn_fwd_bf16_gqa_ws -- attn_fwd_bf16_gqa allowed to split the key range,
+ * as attn_fwd_bf16_ws does for the unmasked call.
+ *
+ * Without a mask the split is attn_fwd_bf16_ws's.  Under a causal mask the
+ * work items (256 query rows of one head) see different numbers of keys; the
+ * last, partly filled round of compute units is split only when the items
+ * are nearly equal (the first q-tile of a head sees at least 3/4 of the key
+ * tiles of its last: a short Sq against a long Sk with the bottom-right
+ * diagonal, the shape of a prefill after cached keys), and a split item cuts
+ * the key tiles its rows see into equal consecutive ranges.  Otherwise the
+ * call runs single-pass (longest items first).  With lse, the rows of split
+ * items get the log-sum-exp of the merged sums.
+ *
+ *   workspace       : at least attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk,
+ *                     mask) bytes, 16-byte aligned, not overlapping q, k, v,
+ *                     o or lse; may be NULL when that size is 0.
+ *   workspace_bytes : its size in bytes.
+ *   other arguments : as attn_fwd_bf16_gqa.
+ *
+ * Status codes as attn_fwd_bf16_gqa, plus those attn_fwd_bf16_ws adds for
+ * the workspace.  Results can differ from attn_fwd_bf16_gqa's in the last
+ * bits where a split happens (the order of the fp32 sums); deterministic for
+ * a given shape and device.  Calls that share a workspace must be ordered on
+ * one stream.
+ */
+int attn_fwd_bf16_gqa_ws(const void *q, const void *k, const void *v, void *o,
+                         float *lse, int64_t B, int64_t H, int64_t H_kv, int64_t Sq,
+                         int64_t Sk, int layout, int round_mode, int mask,
+                         void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_bf16_gqa_workspace_size -- bytes of workspace attn_fwd_bf16_gqa_ws
+ * needs for this shape and mask on the current device (0: it will not
+ * split; the K/V head count does not matter).  Returns ATTN_ERR_NULL,
+ * ATTN_ERR_SIZE, ATTN_ERR_MASK or ATTN_ERR_DEVICE.  Bounded like
+ * attn_fwd_bf16_workspace_size's.
+ */
+int attn_fwd_bf16_gqa_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk,
+                                     int mask, int64_t *bytes);
+
+/*
+ * attn_fwd_bf16_split_plan_masked -- attn_fwd_bf16_gqa_ws's split decision as
+ * a pure function for testing: B*H = n_heads heads of Sq x Sk under `mask`
+ * on n_cu compute units; out4 as attn_fwd_bf16_split_plan's (under a causal
+ * mask the last entry is the heaviest item's tiles per range).  Returns
+ * ATTN_ERR_NULL, ATTN_ERR_SIZE or ATTN_ERR_MASK.
+ */
+int attn_fwd_bf16_split_plan_masked(int64_t n_heads, int64_t Sq, int64_t Sk, int mask,
+                                    int64_t n_cu, int64_t *out4);
 
 /*
  * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs

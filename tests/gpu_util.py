@@ -96,6 +96,29 @@ def launch_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor
     return nbytes
 
 
+def launch_gqa_ws(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, o: torch.Tensor, layout: str, mode: str,
+                  mask: str = "none", lse: torch.Tensor | None = None) -> int:
+    """Call attn_fwd_bf16_gqa_ws through the C ABI with a torch-allocated
+    workspace of the size the library asks for; returns that size."""
+    if layout == "bshd":
+        B, Sq, H, _ = q.shape
+        Sk, H_kv = k.shape[1], k.shape[2]
+    else:
+        B, H, Sq, _ = q.shape
+        H_kv, Sk = k.shape[1], k.shape[2]
+    s = torch.cuda.current_stream()
+    nbytes = attn.attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, attn.MASKS[mask])
+    ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q.device)
+    st = attn.attn_fwd_bf16_gqa_ws(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                   lse.data_ptr() if lse is not None else 0, B, H, H_kv, Sq, Sk,
+                                   attn.LAYOUTS[layout], attn.ROUND_MODES[mode], attn.MASKS[mask], ws.data_ptr(),
+                                   nbytes, s.cuda_stream)
+    if st != 0:
+        raise attn.AttnError(st)
+    torch.cuda.synchronize()
+    return nbytes
+
+
 class Dev:
     """Device copies of one Inputs bundle."""
 

@@ -25,8 +25,9 @@ def _enum_values():
 
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
-    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_masked",
-                     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_strerror", "attn_fwd_bf16_varlen",
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_gqa_workspace_size",
+                     "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_masked", "attn_fwd_bf16_split_plan",
+                     "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror", "attn_fwd_bf16_varlen",
                      "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
@@ -248,3 +249,97 @@ def test_split_plan_argument_errors():
     assert lib.attn_fwd_bf16_split_plan(0, 1, 1, out) == ev["ATTN_ERR_SIZE"]
     assert lib.attn_fwd_bf16_split_plan(1, 0, 1, out) == ev["ATTN_ERR_SIZE"]
     assert lib.attn_fwd_bf16_split_plan(1, 1, 0, out) == ev["ATTN_ERR_SIZE"]
+
+
+W_ = 0x70000  # a fake workspace
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 0, 1, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 0, 1, 4, 3, 1, 1, 0, 0, 1, 0, 0), "ATTN_ERR_HEADS"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 0, 1, 0, 0, 1, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 2, 0, 1, 0, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 3, 1, 0, 0), "ATTN_ERR_ROUND"),
+    ((A, B_, C, O_, L_ + 1, 1, 4, 2, 1, 1, 0, 0, 1, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, O_, O_, 1, 4, 2, 1, 1, 0, 0, 1, 0, 0), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 0, 3, 0, 0), "ATTN_ERR_MASK"),
+    ((A, B_, C, O_, L_, 1, 4, 2, 1, 1, 0, 0, 1, W_, -1), "ATTN_ERR_SIZE"),  # negative workspace size
+])
+def test_gqa_ws_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_gqa_ws(*args, 0) == ev[code]
+
+
+def test_gqa_workspace_size_argument_errors():
+    import ctypes
+
+    lib = attn.load_library()
+    out = ctypes.c_int64(7)
+    ev = _enum_values()
+    assert lib.attn_fwd_bf16_gqa_workspace_size(1, 1, 1, 1, 0, None) == ev["ATTN_ERR_NULL"]
+    assert lib.attn_fwd_bf16_gqa_workspace_size(1, 0, 1, 1, 1, ctypes.byref(out)) == ev["ATTN_ERR_SIZE"]
+    assert out.value == 0
+    assert lib.attn_fwd_bf16_gqa_workspace_size(1, 1, 1, 1, 5, ctypes.byref(out)) == ev["ATTN_ERR_MASK"]
+
+
+def _masked_plan(n_heads, Sq, Sk, mask, n_cu=256):
+    return attn.attn_fwd_bf16_split_plan_masked(n_heads, Sq, Sk, attn.MASKS[mask], n_cu)
+
+
+def _causal_tiles(qt, Sq, Sk, mask):
+    """Key tiles q-tile qt visits, from the mask's definition: up to the last
+    visible key of its last row, at least one."""
+    off = Sk - Sq if mask == "causal_br" else 0
+    last_row = min(Sq, 256 * qt + 256) - 1
+    last_key = min(last_row + off, Sk - 1)
+    return 1 if last_key < 0 else last_key // 64 + 1
+
+
+@pytest.mark.parametrize("n_heads,Sq,Sk", [(48, 4097, 32771), (4, 300, 2000), (24, 512, 1280), (64, 8192, 8192),
+                                           (3, 100, 100), (7, 1000, 300), (10, 256, 64 * 40)])
+def test_masked_plan_without_mask_is_the_plain_plan(n_heads, Sq, Sk):
+    n_qt = -(-Sq // 256)
+    assert _masked_plan(n_heads, Sq, Sk, "none") == _plan(n_heads * n_qt, -(-Sk // 64))
+
+
+@pytest.mark.parametrize("n_heads,Sq,Sk,mask,expect", [
+    (48, 4097, 32771, "causal_br", (768, 48, 5, 103)),  # prefill after 28674 cached keys: items nearly equal
+    (48, 4097, 32771, "causal", (816, 0, 1, 65)),      # top-left: q-tiles see 4 .. 65 tiles, no split
+    (64, 8192, 8192, "causal", (2048, 0, 1, 128)),
+    (24, 512, 1280, "causal_br", (0, 48, 5, 4)),        # q-tiles see 16 and 20 tiles: 5 ranges of the longest
+    (4, 300, 2000, "causal_br", (0, 8, 8, 4)),
+    (4, 2000, 300, "causal_br", (32, 0, 1, 5)),         # Sq > Sk: the first q-tiles see no key
+])
+def test_masked_plan_cases(n_heads, Sq, Sk, mask, expect):
+    assert _masked_plan(n_heads, Sq, Sk, mask) == expect
+
+
+@pytest.mark.parametrize("mask", ["causal", "causal_br"])
+@pytest.mark.parametrize("n_heads", [1, 3, 24, 100, 257])
+@pytest.mark.parametrize("Sq,Sk", [(100, 100), (300, 2000), (512, 1280), (1000, 30000), (4097, 32771), (2000, 300),
+                                   (8192, 8192)])
+def test_masked_plan_invariants(mask, n_heads, Sq, Sk):
+    n_cu = 256
+    n_qt = -(-Sq // 256)
+    whole, items, splits, tps = _masked_plan(n_heads, Sq, Sk, mask, n_cu)
+    tiles = [_causal_tiles(qt, Sq, Sk, mask) for qt in range(n_qt)]
+    assert whole + items == n_heads * n_qt
+    if items == 0:
+        assert splits == 1
+        return
+    assert 4 * min(tiles) >= 3 * max(tiles)  # split only when the items are nearly equal
+    assert whole % n_cu == 0 and 0 < items < n_cu and items * splits <= n_cu
+    assert splits >= 2 and tps >= 4 and (splits - 1) * tps < max(tiles) <= splits * tps
+
+
+def test_masked_plan_argument_errors():
+    import ctypes
+
+    ev = _enum_values()
+    lib = attn.load_library()
+    out = (ctypes.c_int64 * 4)()
+    assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 1, 0, 1, None) == ev["ATTN_ERR_NULL"]
+    assert lib.attn_fwd_bf16_split_plan_masked(0, 1, 1, 0, 1, out) == ev["ATTN_ERR_SIZE"]
+    assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 0, 0, 1, out) == ev["ATTN_ERR_SIZE"]
+    assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 1, 0, 0, out) == ev["ATTN_ERR_SIZE"]
+    assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 1, 3, 1, out) == ev["ATTN_ERR_MASK"]
