@@ -129,10 +129,15 @@ class Dev:
         self.o = torch.empty_like(self.q)
 
     def run(self, mode: str, split: bool = False, mask: str | None = None) -> np.ndarray:
-        """Output bits in the stored layout (split: through attn_fwd_bf16_ws; a
-        mask, or the workload's own, through attn_fwd_bf16_masked)."""
+        """Output bits in the stored layout (split: through attn_fwd_bf16_ws, or
+        attn_fwd_bf16_gqa_ws with a mask or grouped heads; otherwise a mask, or
+        the workload's own, through attn_fwd_bf16_masked, grouped heads through
+        attn_fwd_bf16_gqa)."""
         mask = self.inp.wl.mask if mask is None else mask
-        if self.inp.wl.kv_heads != self.inp.wl.H:
+        grouped = self.inp.wl.kv_heads != self.inp.wl.H
+        if split and (grouped or mask != "none"):
+            launch_gqa_ws(self.q, self.k, self.v, self.o, self.layout, mode, mask)
+        elif grouped:
             launch_gqa(self.q, self.k, self.v, self.o, self.layout, mode, mask)
         elif mask != "none":
             launch_masked(self.q, self.k, self.v, self.o, self.layout, mode, mask)

@@ -1,5 +1,6 @@
-"""GPU parity at the full workload sizes, in the launch configuration the
-benchmark times (one attn_fwd_bf16 call over the whole tensor).
+"""GPU parity at the full workload sizes, in the launch configurations the
+benchmark times (one call over the whole tensor: the single pass, and the
+key-range split where the shape splits).
 
 The oracle computes sampled rows one by one: seeded random rows of every
 head, plus the rows that sit on tile boundaries and at the ragged end of the
@@ -79,8 +80,12 @@ def _run_config(name):
     # determinism over the whole tensor
     again = dev.run(wl.modes[0])
     assert np.array_equal(again, outs[wl.modes[0]]), "repeated launch changed the output"
-    # the key-range-splitting entry point, where this shape splits
-    if wl.mask == "none" and wl.kv_heads == wl.H and attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk) > 0:
+    # the key-range-splitting entry point, where this shape splits (the call the benchmark times then)
+    if wl.mask == "none" and wl.kv_heads == wl.H:
+        split_bytes = attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
+    else:
+        split_bytes = attn.attn_fwd_bf16_gqa_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk, attn.MASKS[wl.mask])
+    if split_bytes > 0:
         for mode in wl.modes:
             out = dev.run(mode, split=True)
             res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
