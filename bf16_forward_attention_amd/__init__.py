@@ -14,6 +14,9 @@ only, every step of the computation runs in the HIP library
     attn_fwd_bf16_gqa_ws(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, ws, ws_bytes,
                          stream) -> status
     attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, mask) -> bytes
+    attn_fwd_bf16_partial(q, k, v, o_part, lse_part, B, H, H_kv, Sq, Sk, key_offset, Sk_total, layout, mask,
+                          stream) -> status
+    attn_fwd_bf16_merge(o_parts, lse_parts, n_parts, o, lse, B, H, Sq, layout, round_mode, stream) -> status
     attn_fwd_bf16_split_plan(n_work, n_tiles, n_cu) -> (whole, split items, splits, tiles per split)
     attn_fwd_bf16_split_plan_masked(n_heads, Sq, Sk, mask, n_cu) -> the same four numbers
     attn_fwd(q, k, v, out=None, layout="bshd", round_mode="rtne", split=True, mask="none") -> torch.Tensor
@@ -28,7 +31,7 @@ import os
 __all__ = [
     "attn_fwd_bf16", "attn_fwd_bf16_masked", "attn_fwd_bf16_gqa", "attn_fwd_bf16_varlen", "attn_fwd_bf16_ws",
     "attn_fwd_varlen", "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_gqa_workspace_size",
-    "attn_fwd_bf16_split_plan", "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
+    "attn_fwd_bf16_split_plan", "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_partial", "attn_fwd_bf16_merge", "attn_fwd_bf16_strerror", "attn_fwd_bf16_abi_version", "attn_fwd",
     "AttnError", "LAYOUTS", "ROUND_MODES", "MASKS", "library_path", "load_library",
 ]
 
@@ -90,6 +93,11 @@ def load_library():
         lib.attn_fwd_bf16_gqa_workspace_size.restype = ctypes.c_int
         lib.attn_fwd_bf16_split_plan_masked.argtypes = [i64, i64, i64, ctypes.c_int, i64, ctypes.POINTER(i64)]
         lib.attn_fwd_bf16_split_plan_masked.restype = ctypes.c_int
+        lib.attn_fwd_bf16_partial.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, i64, i64, ctypes.c_int,
+                                              ctypes.c_int, vp]
+        lib.attn_fwd_bf16_partial.restype = ctypes.c_int
+        lib.attn_fwd_bf16_merge.argtypes = [vp, vp, i64, vp, vp, i64, i64, i64, ctypes.c_int, ctypes.c_int, vp]
+        lib.attn_fwd_bf16_merge.restype = ctypes.c_int
         lib.attn_fwd_bf16_strerror.argtypes = [ctypes.c_int]
         lib.attn_fwd_bf16_strerror.restype = ctypes.c_char_p
         lib.attn_fwd_bf16_abi_version.argtypes = []
@@ -169,6 +177,20 @@ def attn_fwd_bf16_split_plan_masked(n_heads: int, Sq: int, Sk: int, mask: int, n
     if status != 0:
         raise AttnError(status)
     return tuple(out)
+
+
+def attn_fwd_bf16_partial(q: int, k: int, v: int, o_part: int, lse_part: int, B: int, H: int, H_kv: int, Sq: int,
+                          Sk: int, key_offset: int, Sk_total: int, layout: int, mask: int, stream: int) -> int:
+    """One key shard's fp32 rows and log-sum-exp (raw device addresses); returns the status code."""
+    return load_library().attn_fwd_bf16_partial(q, k, v, o_part or None, lse_part or None, B, H, H_kv, Sq, Sk,
+                                                key_offset, Sk_total, layout, mask, stream)
+
+
+def attn_fwd_bf16_merge(o_parts: int, lse_parts: int, n_parts: int, o: int, lse: int, B: int, H: int, Sq: int,
+                        layout: int, round_mode: int, stream: int) -> int:
+    """Merge of key-shard partials into the bf16 output (lse 0: not written); returns the status code."""
+    return load_library().attn_fwd_bf16_merge(o_parts or None, lse_parts or None, n_parts, o or None, lse or None,
+                                              B, H, Sq, layout, round_mode, stream)
 
 
 def attn_fwd_bf16_split_plan(n_work: int, n_tiles: int, n_cu: int):

@@ -96,6 +96,7 @@ namespace {
 constexpr int D = 128;
 constexpr int BM = 256;                // query rows per workgroup
 constexpr int BN = 64;                 // keys per tile
+constexpr int kPartial = 3;            // MODE of the instantiation that stores fp32 rows of one key shard
 // The tile loads address the 64 K/V rows of a tile with 32-bit buffer
 // offsets: 63 row strides + 256 bytes must stay below 2^32.  The row stride is
 // H_kv * 256 bytes in BSHD and packed layouts, so H_kv (and H >= H_kv) is
@@ -230,8 +231,9 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // variable-length batch; Sq and Sk are the sequence's own, and items past a
 // sequence's last q-tile exit at once.
 // CAUSAL: query row r attends to the keys
-// j <= min(r + causal_off, Sk - 1) only, causal_off = 0, or Sk - Sq with
-// causal_br.  The workgroup visits the key tiles
+// j <= min(r + causal_off, Sk - 1) only: causal_off_fixed (the host's 0, Sk - Sq,
+// or a key shard's offset from the global diagonal), or with VARLEN 0 or the
+// sequence's Sk - Sq (causal_br).  The workgroup visits the key tiles
 // 0 .. up to its last row's limit in order (so the q-tiles of a head stream
 // the same tiles together, as without a mask): those every row sees whole in
 // a loop without mask code, then the diagonal ones (some row's limit falls
@@ -242,7 +244,7 @@ template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
     uint16_t* __restrict__ O, int H, int Sq_all, int Sk_all, int n_qtiles, Geometry g, Split sp, Varlen vl,
-    int causal_br, float* __restrict__ lse) {
+    int causal_br, int64_t causal_off_fixed, float* __restrict__ lse) {
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
   __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     if (qt * BM >= Sq) return;  // past the sequence's last q-tile (the whole workgroup leaves)
   }
   const int n_tiles_all = (Sk + BN - 1) / BN;
-  const int causal_off = causal_br ? Sk - Sq : 0;
+  const int64_t causal_off = VARLEN ? (causal_br ? Sk - Sq : 0) : causal_off_fixed;
   const uint16_t* Qh = Q + q_base + h * g.q_head;
   const int hk = h / (int)g.kv_group;
   const uint16_t* Kh = K + k_base + hk * g.k_head;
@@ -414,7 +416,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   if constexpr (CAUSAL) {
     const int64_t last_key = (int64_t)Sk - 1;
     const int64_t lim = (int64_t)qrow + causal_off;
-    row_lim = (int)(lim < last_key ? lim : last_key);
+    row_lim = (int)(lim < last_key ? (lim < -1 ? -1 : lim) : last_key);  // -1: no key
     const int64_t r_last = ((int64_t)qt * BM + BM < Sq ? (int64_t)qt * BM + BM : (int64_t)Sq) - 1;
     const int64_t hi = r_last + causal_off < last_key ? r_last + causal_off : last_key;
     n_tiles = hi < 0 ? 1 : (int)(hi / BN) + 1;
@@ -717,6 +719,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // sum_j 2^t_j = 2^m l, so ln(sum_j exp(s_j / sqrt(128))) = ln(2) (m + log2 l)
   // (l = 0: -Inf; l NaN: NaN)
   if (lse && grp == 0 && qrow < Sq) lse[lse_row0 + qrow] = (m_run + log2f(l_tot)) * 0.6931471805599453f;
+  if constexpr (MODE == kPartial) {
+    // one key shard's rows in fp32, normalised by the shard's own sum (rows
+    // that see no key of the shard: 0, with an lse of -Inf)
+    const float inv_p = l_tot == 0.0f ? 0.0f : 1.0f / l_tot;
+    if (qrow < Sq) {
+      float* dst = (float*)O + q_base + h * g.q_head + (int64_t)qrow * g.q_row + 4 * grp;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          *(f32x4*)(dst + 32 * db + 8 * r) = f32x4{acc[db][4 * r] * inv_p, acc[db][4 * r + 1] * inv_p,
+                                                   acc[db][4 * r + 2] * inv_p, acc[db][4 * r + 3] * inv_p};
+    }
+    return;
+  }
   // normalise, round, store this lane's query row
   const float inv_l = 1.0f / l_tot;
   if (qrow < Sq) {
@@ -775,6 +792,59 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
   const uint32_t lo = round_to_bf16<MODE>(num[0] * inv) | ((uint32_t)round_to_bf16<MODE>(num[1] * inv) << 16);
   const uint32_t hi = round_to_bf16<MODE>(num[2] * inv) | ((uint32_t)round_to_bf16<MODE>(num[3] * inv) << 16);
   *(u32x2*)dst = u32x2{lo, hi};
+}
+
+// Combines the key-shard partials of attn_fwd_bf16_partial: per query row,
+// M = max_s lse_s, w_s = exp(lse_s - M), O = (sum_s w_s O_s) / (sum_s w_s)
+// and lse = M + ln(sum_s w_s), summed in shard order, then the one rounding
+// to bf16.  One thread per (row, 4 dims); rows are (b, h, i) in row-major
+// order, the shards' rows and O at q's element offsets.  A NaN lse in any
+// shard makes the row NaN (lse NaN); when no shard has a key for the row
+// (every lse -Inf) the row is NaN, the 0/0 of an empty softmax, and its lse
+// -Inf.
+template <int MODE>
+__global__ __launch_bounds__(256) void attn_merge_shards_kernel(const float* __restrict__ parts,
+                                                                const float* __restrict__ lse_parts, int n_parts,
+                                                                int64_t part_elems, int64_t rows, int H, int Sq,
+                                                                Geometry g, uint16_t* __restrict__ O,
+                                                                float* __restrict__ lse) {
+  const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= rows * (D / 4)) return;
+  const int c4 = (int)(gid % (D / 4));
+  const int64_t row = gid / (D / 4);
+  const int i = (int)(row % Sq);
+  const int64_t bh = row / Sq;
+  const int h = (int)(bh % H);
+  const int64_t b = bh / H;
+  const int64_t off = b * g.q_batch + h * g.q_head + (int64_t)i * g.q_row + 4 * c4;
+  float mmax = -__builtin_inff();
+  bool nan = false;
+  for (int s = 0; s < n_parts; ++s) {
+    const float x = lse_parts[(int64_t)s * rows + row];
+    nan |= x != x;
+    mmax = fmaxf(mmax, x);
+  }
+  f32x4 num = {0.0f, 0.0f, 0.0f, 0.0f};
+  float den = 0.0f, lse_row;
+  if (nan || mmax == -__builtin_inff()) {
+    const float qnan = __builtin_nanf("");
+    num = f32x4{qnan, qnan, qnan, qnan};
+    den = 1.0f;
+    lse_row = nan ? qnan : -__builtin_inff();
+  } else {
+    for (int s = 0; s < n_parts; ++s) {
+      const float w = __builtin_amdgcn_exp2f((lse_parts[(int64_t)s * rows + row] - mmax) * 1.4426950408889634f);
+      const f32x4 o = *(const f32x4*)(parts + (int64_t)s * part_elems + off);
+      num += w * o;
+      den += w;
+    }
+    lse_row = mmax + log2f(den) * 0.6931471805599453f;
+  }
+  if (lse && c4 == 0) lse[row] = lse_row;
+  const float inv = 1.0f / den;
+  const uint32_t lo = round_to_bf16<MODE>(num[0] * inv) | ((uint32_t)round_to_bf16<MODE>(num[1] * inv) << 16);
+  const uint32_t hi = round_to_bf16<MODE>(num[2] * inv) | ((uint32_t)round_to_bf16<MODE>(num[3] * inv) << 16);
+  *(u32x2*)(O + off) = u32x2{lo, hi};
 }
 
 // ---------------------------------------------------------------------------
@@ -917,26 +987,27 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
             int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg, int n_split_items,
             int mask, float* lse, hipStream_t s) {
   const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
+  const int64_t off = br ? (int64_t)Sk - Sq : 0;  // fixed-length calls: row i sees keys j <= i + off
   const Varlen none{nullptr, nullptr, 0, 0, 0};
   const dim3 grid((unsigned)n_wg), block(NTHREADS);
   if (n_split_items > 0 && mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, br, lse);
+                       n_qtiles, g, sp, none, 0, off, lse);
   else if (n_split_items > 0)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, lse);
+                       n_qtiles, g, sp, none, 0, (int64_t)0, lse);
   else if (vl && mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, br, lse);
+                       n_qtiles, g, sp, *vl, br, (int64_t)0, lse);
   else if (vl)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, 0, lse);
+                       n_qtiles, g, sp, *vl, 0, (int64_t)0, lse);
   else if (mask != ATTN_MASK_NONE)
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, br, lse);
+                       n_qtiles, g, sp, none, 0, off, lse);
   else
     hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, lse);
+                       n_qtiles, g, sp, none, 0, (int64_t)0, lse);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
     hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
@@ -1068,6 +1139,93 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
   return run(q, k, v, o, H, H_kv, max_seqlen_q, 1, ATTN_LAYOUT_BSHD, round_mode, mask, pb, whole, nullptr, stream,
              &vl, lse);
+}
+
+extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
+                                     int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int64_t key_offset,
+                                     int64_t Sk_total, int layout, int mask, void* stream) {
+  Problem pb;
+  const int st = check_args(q, k, v, o_part, B, H, H_kv, Sq, Sk, layout, ATTN_ROUND_RTNE, &pb);
+  if (st != ATTN_OK) return st;
+  if (!lse_part) return ATTN_ERR_NULL;
+  if (key_offset < 0 || Sk_total > INT32_MAX || key_offset > Sk_total - Sk) return ATTN_ERR_SIZE;
+  if ((uintptr_t)lse_part & 3) return ATTN_ERR_ALIGN;
+  // fp32 rows: twice q's bytes; the lse: a 64th of q's bytes
+  const int64_t o_bytes = 2 * pb.bytes_q, lse_bytes = pb.bytes_q / 64;
+  if (overlaps(o_part, o_bytes, q, pb.bytes_q) || overlaps(o_part, o_bytes, k, pb.bytes_k) ||
+      overlaps(o_part, o_bytes, v, pb.bytes_k) || overlaps(lse_part, lse_bytes, q, pb.bytes_q) ||
+      overlaps(lse_part, lse_bytes, k, pb.bytes_k) || overlaps(lse_part, lse_bytes, v, pb.bytes_k) ||
+      overlaps(lse_part, lse_bytes, o_part, o_bytes))
+    return ATTN_ERR_ALIAS;
+  if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
+    return ATTN_ERR_MASK;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  // row i sees the global keys j <= i + off_global; this shard's key j is
+  // global key key_offset + j
+  const int64_t off_global = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT ? Sk_total - Sq : 0;
+  const int64_t off = off_global - key_offset;
+  const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
+  const Split sp{(int)pb.n_work, 1, (int)pb.n_tiles, nullptr, nullptr};
+  const Varlen none{nullptr, nullptr, 0, 0, 0};
+  const dim3 grid((unsigned)pb.n_work), block(NTHREADS);
+  const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
+  uint16_t* oo = (uint16_t*)o_part;
+  hipStream_t s = (hipStream_t)stream;
+  if (mask == ATTN_MASK_NONE)
+    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
+                       (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, (int64_t)0, lse_part);
+  else
+    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, true, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
+                       (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, off, lse_part);
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+}
+
+extern "C" int attn_fwd_bf16_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o,
+                                   float* lse, int64_t B, int64_t H, int64_t Sq, int layout, int round_mode,
+                                   void* stream) {
+  if (!o_parts || !lse_parts || !o) return ATTN_ERR_NULL;
+  int64_t bh, rows, part_bytes, all_parts, lse_all, o_bytes;
+  if (n_parts < 1 || B < 1 || H < 1 || Sq < 1 || n_parts > INT32_MAX || Sq > INT32_MAX || H > kMaxHeads ||
+      !mul_ok(B, H, &bh) || !mul_ok(bh, Sq, &rows) || !mul_ok(rows, 4 * D, &part_bytes) ||
+      !mul_ok(part_bytes, n_parts, &all_parts) || !mul_ok(rows * 4, n_parts, &lse_all) ||
+      rows > (int64_t(1) << 35))  // the grid of rows * 32 threads in 256-thread blocks fits 32 bits
+    return ATTN_ERR_SIZE;
+  o_bytes = part_bytes / 2;
+  if (layout != ATTN_LAYOUT_BSHD && layout != ATTN_LAYOUT_BHSD) return ATTN_ERR_LAYOUT;
+  if (round_mode != ATTN_ROUND_RTNE && round_mode != ATTN_ROUND_RTNA && round_mode != ATTN_ROUND_RTZ)
+    return ATTN_ERR_ROUND;
+  if ((((uintptr_t)o_parts | (uintptr_t)o) & 15) || (((uintptr_t)lse_parts | (uintptr_t)lse) & 3))
+    return ATTN_ERR_ALIGN;
+  if (overlaps(o, o_bytes, o_parts, all_parts) || overlaps(o, o_bytes, lse_parts, lse_all) ||
+      (lse && (overlaps(lse, rows * 4, o_parts, all_parts) || overlaps(lse, rows * 4, lse_parts, lse_all) ||
+               overlaps(lse, rows * 4, o, o_bytes))))
+    return ATTN_ERR_ALIAS;
+  int n_cu = 0;
+  const int dev_status = check_device(&n_cu);
+  if (dev_status != ATTN_OK) return dev_status;
+  const Geometry g = make_geometry(H, H, Sq, 1, layout);
+  const int64_t threads = rows * (D / 4);
+  const dim3 grid((unsigned)((threads + 255) / 256)), block(256);
+  hipStream_t s = (hipStream_t)stream;
+  uint16_t* oo = (uint16_t*)o;
+  const int64_t part_elems = rows * D;
+  switch (round_mode) {
+    case ATTN_ROUND_RTNE:
+      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTNE>, grid, block, 0, s, o_parts, lse_parts,
+                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      break;
+    case ATTN_ROUND_RTNA:
+      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTNA>, grid, block, 0, s, o_parts, lse_parts,
+                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      break;
+    default:
+      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTZ>, grid, block, 0, s, o_parts, lse_parts,
+                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      break;
+  }
+  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {

@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 7
+#define ATTN_FWD_ABI_VERSION 8
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -288,6 +288,70 @@ int attn_fwd_bf16_gqa_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t S
  */
 int attn_fwd_bf16_split_plan_masked(int64_t n_heads, int64_t Sq, int64_t Sk, int mask,
                                     int64_t n_cu, int64_t *out4);
+
+/*
+ * attn_fwd_bf16_partial -- attention of the query rows over one shard of the
+ * keys, for key (context) parallelism: the keys of each head are cut into
+ * shards that are processed apart (on other devices, or one after another)
+ * and combined by attn_fwd_bf16_merge, which rounds once.
+ *
+ * The pages do not treat this; it follows from the row's softmax being a
+ * sum over keys: a shard's rows normalised by the shard's own sum, with the
+ * shard's log-sum-exp (attn_fwd_bf16_gqa's lse), are all a merge needs (the
+ * FlashAttention family's out + softmax_lse per key block).
+ *
+ *   q          : [B, Sq, H, 128] (BSHD) or [B, H, Sq, 128] (BHSD) bf16.
+ *   k, v       : this shard, [B, Sk, H_kv, 128] or [B, H_kv, Sk, 128]:
+ *                global keys key_offset .. key_offset + Sk - 1 of a head
+ *                with Sk_total keys.
+ *   o_part     : B*H*Sq*128 fp32 at q's element offsets (q's layout), 16-byte
+ *                aligned: the shard's rows, sum_j w_j v_j / sum_j w_j over the
+ *                shard's visible keys; 0 for a row that sees none of them.
+ *   lse_part   : B*H*Sq fp32 laid out [B, H, Sq], 4-byte aligned, required:
+ *                ln sum_j exp(q.k_j / sqrt(128)) over the shard's visible
+ *                keys; -Inf for a row that sees none of them, NaN where a
+ *                logit is NaN or +Inf.
+ *   key_offset, Sk_total : the shard's place, 0 <= key_offset,
+ *                key_offset + Sk <= Sk_total <= 2^31 - 1.
+ *   mask       : attn_mask_t over the global keys: ATTN_MASK_CAUSAL (row i
+ *                sees global keys j <= i) or ATTN_MASK_CAUSAL_BOTTOM_RIGHT
+ *                (j <= i + Sk_total - Sq).
+ *   other arguments : as attn_fwd_bf16_gqa.
+ *
+ * Status codes as attn_fwd_bf16_gqa (ATTN_ERR_NULL also for lse_part,
+ * ATTN_ERR_SIZE for a shard outside [0, Sk_total), ATTN_ERR_ALIGN /
+ * ATTN_ERR_ALIAS for o_part and lse_part).  Single pass, deterministic.
+ */
+int attn_fwd_bf16_partial(const void *q, const void *k, const void *v, float *o_part,
+                          float *lse_part, int64_t B, int64_t H, int64_t H_kv, int64_t Sq,
+                          int64_t Sk, int64_t key_offset, int64_t Sk_total, int layout,
+                          int mask, void *stream);
+
+/*
+ * attn_fwd_bf16_merge -- combines n_parts shard results of
+ * attn_fwd_bf16_partial into the bf16 output: per row, M = max_s lse_s,
+ * w_s = exp(lse_s - M), O = sum_s w_s O_s / sum_s w_s (in shard order, fp32),
+ * then one rounding in round_mode; lse (optional) = M + ln sum_s w_s.
+ *
+ *   o_parts    : n_parts consecutive fp32 arrays of B*H*Sq*128 values (each
+ *                at q's element offsets in `layout`), 16-byte aligned.
+ *   lse_parts  : n_parts consecutive fp32 [B, H, Sq] arrays, 4-byte aligned.
+ *   o          : bf16 output shaped like q, 16-byte aligned.
+ *   lse        : NULL, or B*H*Sq fp32 [B, H, Sq]: the row's log-sum-exp over
+ *                all shards.
+ *   B, H, Sq, layout, round_mode, stream : as attn_fwd_bf16.
+ *
+ * A row that no shard gives a key (every lse_s -Inf) is NaN with an lse of
+ * -Inf; a NaN lse_s makes the row and its lse NaN.  Merging the shards of a
+ * cut of the keys gives the whole-key result within the same tolerance of
+ * the exact result (not necessarily the same bits: the sums run in another
+ * order).  Status codes: ATTN_ERR_NULL, ATTN_ERR_SIZE (n_parts < 1, sizes),
+ * ATTN_ERR_LAYOUT, ATTN_ERR_ROUND, ATTN_ERR_ALIGN, ATTN_ERR_ALIAS (o or lse
+ * overlapping the parts or each other), ATTN_ERR_DEVICE, ATTN_ERR_HIP.
+ */
+int attn_fwd_bf16_merge(const float *o_parts, const float *lse_parts, int64_t n_parts,
+                        void *o, float *lse, int64_t B, int64_t H, int64_t Sq, int layout,
+                        int round_mode, void *stream);
 
 /*
  * attn_fwd_bf16_workspace_size -- bytes of workspace attn_fwd_bf16_ws needs

@@ -26,8 +26,9 @@ def _enum_values():
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
     assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_gqa_workspace_size",
-                     "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_masked", "attn_fwd_bf16_split_plan",
-                     "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror", "attn_fwd_bf16_varlen",
+                     "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_masked", "attn_fwd_bf16_merge", "attn_fwd_bf16_partial",
+                     "attn_fwd_bf16_split_plan", "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror",
+                     "attn_fwd_bf16_varlen",
                      "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
     out = subprocess.run(["nm", "-D", "--defined-only", attn.library_path()], capture_output=True, text=True,
                          check=True).stdout
@@ -343,3 +344,51 @@ def test_masked_plan_argument_errors():
     assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 0, 0, 1, out) == ev["ATTN_ERR_SIZE"]
     assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 1, 0, 0, out) == ev["ATTN_ERR_SIZE"]
     assert lib.attn_fwd_bf16_split_plan_masked(1, 1, 1, 3, 1, out) == ev["ATTN_ERR_MASK"]
+
+
+P_ = 0x80000  # a fake fp32 partial output (4 heads x 2 rows x 512 B = 4 KiB)
+PL = 0x90000  # a fake partial lse
+
+
+@pytest.mark.parametrize("args,code", [
+    # q, k, v, o_part, lse_part, B, H, H_kv, Sq, Sk, key_offset, Sk_total, layout, mask
+    ((0, B_, C, P_, PL, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, 0, PL, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, P_, 0, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_NULL"),
+    ((A, B_, C, P_, PL, 1, 4, 3, 2, 8, 0, 8, 0, 0), "ATTN_ERR_HEADS"),
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, -1, 8, 0, 0), "ATTN_ERR_SIZE"),     # shard before the first key
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, 1, 8, 0, 0), "ATTN_ERR_SIZE"),      # shard past the last key
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, 0, 1 << 31, 0, 0), "ATTN_ERR_SIZE"),
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, 0, 8, 3, 0), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, P_ + 8, PL, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, P_, PL + 2, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, P_, P_ + 2048, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_ALIAS"),  # lse inside the fp32 rows
+    ((A, B_, C, A - 2048, PL, 1, 4, 2, 2, 8, 0, 8, 0, 0), "ATTN_ERR_ALIAS"),  # fp32 rows (2x q's bytes) reach q
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, 0, 8, 0, 4), "ATTN_ERR_MASK"),
+    ((A, B_, C, P_, PL, 1, 4, 2, 2, 8, 2, 10, 0, 4), "ATTN_ERR_MASK"),    # a shard in the middle passes the checks
+])
+def test_partial_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_partial(*args, 0) == ev[code]
+
+
+@pytest.mark.parametrize("args,code", [
+    # o_parts, lse_parts, n_parts, o, lse, B, H, Sq, layout, round_mode
+    ((0, PL, 2, O_, 0, 1, 4, 2, 0, 0), "ATTN_ERR_NULL"),
+    ((P_, 0, 2, O_, 0, 1, 4, 2, 0, 0), "ATTN_ERR_NULL"),
+    ((P_, PL, 2, 0, 0, 1, 4, 2, 0, 0), "ATTN_ERR_NULL"),
+    ((P_, PL, 0, O_, 0, 1, 4, 2, 0, 0), "ATTN_ERR_SIZE"),
+    ((P_, PL, 2, O_, 0, 1, 0, 2, 0, 0), "ATTN_ERR_SIZE"),
+    ((P_, PL, 2, O_, 0, 1 << 40, 1 << 18, 2, 0, 0), "ATTN_ERR_SIZE"),
+    ((P_, PL, 2, O_, 0, 1, 4, 2, 2, 0), "ATTN_ERR_LAYOUT"),
+    ((P_, PL, 2, O_, 0, 1, 4, 2, 0, 3), "ATTN_ERR_ROUND"),
+    ((P_ + 4, PL, 2, O_, 0, 1, 4, 2, 0, 0), "ATTN_ERR_ALIGN"),
+    ((P_, PL, 2, O_ + 8, 0, 1, 4, 2, 0, 0), "ATTN_ERR_ALIGN"),
+    ((P_, PL, 2, O_, L_ + 1, 1, 4, 2, 0, 0), "ATTN_ERR_ALIGN"),
+    ((P_, PL, 2, P_ + 4096, 0, 1, 4, 2, 0, 0), "ATTN_ERR_ALIAS"),     # o over the second part
+    ((P_, PL, 2, O_, PL + 32, 1, 4, 2, 0, 0), "ATTN_ERR_ALIAS"),      # lse over the second part's lse
+    ((P_, PL, 2, O_, O_ + 64, 1, 4, 2, 0, 0), "ATTN_ERR_ALIAS"),      # lse inside o
+])
+def test_merge_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_merge(*args, 0) == ev[code]
