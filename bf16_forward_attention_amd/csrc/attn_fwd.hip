@@ -25,7 +25,15 @@
 // the items of that round can run as several workgroups over consecutive key
 // ranges; each leaves unnormalised fp32 rows with their running maximum and
 // sum, and attn_merge_kernel combines them (the same max-shifted sums as the
-// online softmax) before the one rounding to bf16.
+// online softmax) before the one rounding to bf16.  Under a causal mask this
+// is done only when the items are nearly equal, each split item cutting its
+// own visible tiles into equal ranges.
+//
+// Key shards.  The kPartial instantiation computes the rows over one shard
+// of a head's keys (its causal diagonal given relative to the shard) and
+// stores them in fp32, normalised by the shard's own sum, with the shard's
+// log-sum-exp; attn_merge_shards_kernel combines shards by their
+// log-sum-exps and rounds once: the per-device part of key parallelism.
 //
 // Extensions the pages list as missing from the kernel they describe (their
 // section "Hvad er udgivet" / What was released): a causal mask (CAUSAL: the
