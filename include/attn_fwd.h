@@ -9,7 +9,8 @@
  *
  * without a mask (attn_fwd_bf16_masked adds a causal one), head_dim fixed at
  * 128, one head count shared by Q, K and V (attn_fwd_bf16_gqa allows fewer
- * K/V heads; attn_fwd_bf16_varlen takes packed sequences of their own lengths), any
+ * K/V heads; attn_fwd_bf16_varlen takes packed sequences of their own lengths;
+ * attn_fwd_bf16_partial and attn_fwd_bf16_merge cut the keys into shards), any
  * query length Sq and key length Sk (cross-attention allowed), inputs read in
  * the BSHD or BHSD layout without a transpose (same page, section "Hvad er
  * udgivet" / What was released).  Output is bf16, rounded per call in one of
