@@ -494,7 +494,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 
   f32x16 S[2][2];      // logits of two tiles: the one being turned into weights, the next one
   bf16x8 pf[2][2];     // weights of the current tile, the B operand of P.V
-  float mx = 0.0f;     // row maximum of the next tile's logits
+  float mx = 0.0f;     // maximum of the next tile's logits over this lane's half of the row
 
   // S^T = K . Q^T for the two 32-key blocks of one tile (K stage kt)
   auto qk = [&](f32x16 (&s)[2], const uint8_t* kt) __attribute__((always_inline)) {
@@ -533,9 +533,12 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int n = 0; n < 16; ++n) m = fmaxf(m, s[kb][n]);
-    mx = wave_half_max(m);
+    mx = m;
   };
-  // Move the running maximum when some row's maximum grew past 2^8.  The
+  // Move the running maximum when some row's maximum grew past 2^8.  Whether
+  // any row did is decided from each lane's half of its row (a row's maximum
+  // grew past the threshold iff one of its halves did), so the exchange
+  // between the two halves is only needed on the rare move itself.  The
   // candidate is the scaled row maximum rounded up by at least half an ulp:
   // then fma(s, c, -m) <= 0 for the maximal logit, its weight exp2(<= 0) <= 1
   // rounds to exactly 1 in bf16, so a row dominated by one key (or with a
@@ -543,8 +546,10 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // give NaN here, which fmaxf ignores.)
   auto rescale = [&]() __attribute__((always_inline)) {
     const float ms = mx * kScaleLog2;
-    const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(ms), 0x1p-23f, ms));
-    if (__builtin_amdgcn_ballot_w64(m_new > m_run + kRescaleLog2) != 0) {
+    const float m_half = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(ms), 0x1p-23f, ms));
+    if (__builtin_amdgcn_ballot_w64(m_half > m_run + kRescaleLog2) != 0) {
+      const float mr = wave_half_max(mx) * kScaleLog2;
+      const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(mr), 0x1p-23f, mr));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
       l_run *= alpha;
@@ -616,7 +621,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
       m = fmaxf(m, sn[i >> 3][2 * (i & 7)]);
       m = fmaxf(m, sn[i >> 3][2 * (i & 7) + 1]);
     }
-    mx = wave_half_max(m);
+    mx = m;
   };
 
   // ---- main loop: four LDS stages, tiles loaded three ahead, one barrier per tile ----
