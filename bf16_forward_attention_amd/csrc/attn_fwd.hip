@@ -613,13 +613,21 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
       acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i], pf[kb][hh], acc[db], 0, 0, 0);
       if (i == kHookAt0) hook(0);
       if (i == kHookAt1) hook(1);
-      if (MASKED) {
+      {
+        // (a select into a temporary written back whole: the same mask as a
+        // conditional store into the accumulator made this compiler emit about
+        // 270 selects per tile instead of 32, and use 102 scalar registers)
         const int n = 2 * (i & 7), key = 32 * (i >> 3) + n;
-        if (key > rel) sn[i >> 3][n] = -__builtin_inff();
-        if (key + 1 > rel) sn[i >> 3][n + 1] = -__builtin_inff();
+        float x0 = sn[i >> 3][n], x1 = sn[i >> 3][n + 1];
+        if (MASKED) {
+          x0 = key > rel ? -__builtin_inff() : x0;
+          x1 = key + 1 > rel ? -__builtin_inff() : x1;
+          sn[i >> 3][n] = x0;
+          sn[i >> 3][n + 1] = x1;
+        }
+        m = fmaxf(m, x0);
+        m = fmaxf(m, x1);
       }
-      m = fmaxf(m, sn[i >> 3][2 * (i & 7)]);
-      m = fmaxf(m, sn[i >> 3][2 * (i & 7) + 1]);
     }
     mx = m;
   };
