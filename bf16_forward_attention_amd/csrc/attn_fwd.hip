@@ -321,7 +321,9 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   const int n_tiles_all = (Sk + BN - 1) / BN;
   const int64_t causal_off = VARLEN ? (causal_br ? Sk - Sq : 0) : causal_off_fixed;
   const uint16_t* Qh = Q + q_base + h * g.q_head;
-  const int hk = h / (int)g.kv_group;
+  // (the integer division runs on the vector unit; made uniform again so that
+  // the K/V pointers, and the per-tile addresses formed from them, stay scalar)
+  const int hk = __builtin_amdgcn_readfirstlane(h / (int)g.kv_group);
   const uint16_t* Kh = K + k_base + hk * g.k_head;
   const uint16_t* Vh = V + k_base + hk * g.k_head;
   uint16_t* Oh = O + q_base + h * g.q_head;
