@@ -5,8 +5,8 @@ A step is one call of the library over the whole workload (every query row of
 every head), inputs resident in HBM: attn_fwd_bf16_ws with a preallocated
 workspace when the shape splits its key ranges (then the step is both of its
 kernels; attn_fwd_bf16_gqa_ws for the causal and grouped-query workloads),
-attn_fwd_bf16_gqa for grouped-query or causal workloads that do not split,
-attn_fwd_bf16 otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
+attn_fwd_bf16_gqa (grouped) or attn_fwd_bf16_masked (causal) for those that
+do not split, attn_fwd_bf16 otherwise.  Default workload: self-attention B=4, H=16, Sq=Sk=8192, d=128,
 BSHD, RTNE.  Prints one JSON line:
 
   value      forward TFLOP/s, 4*128 FLOPs per visible (query, key) pair (all
