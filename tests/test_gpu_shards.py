@@ -195,3 +195,34 @@ def test_nan_and_inf_keys_through_the_merge():
     assert nan_rows[0, 0].all() and nan_rows[0, 1].any() and not nan_rows[0, 1].all()
     assert nan_rows[0, 2].any() and not nan_rows[0, 2].all()
     assert np.array_equal(np.isnan(lse.cpu().numpy()), nan_rows)
+
+
+def test_shards_far_along_a_long_sequence():
+    # A shard of 1000 keys at the end of a sequence of 2^31 - 1 keys (only the shard is allocated):
+    # with the top-left diagonal no row of a short query block sees any of its keys (the offset
+    # from the diagonal is about -2^31: 0 rows and an lse of -Inf); with the bottom-right one the
+    # last shard sees exactly what a bottom-right call on the shard alone sees, so its single-shard
+    # merge gives that call's bits.
+    B, H, Sq, Sk = 1, 2, 300, 1000
+    total = (1 << 31) - 1
+    inp = synth.small(B, H, Sq, Sk, "bshd", seed=44)
+    q, k, v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+    s = torch.cuda.current_stream().cuda_stream
+    for mask in ("causal", "causal_br"):
+        o_part = torch.full((1,) + tuple(q.shape), 7.0, dtype=torch.float32, device="cuda:0")
+        lse_part = torch.full((1, B, H, Sq), 7.0, dtype=torch.float32, device="cuda:0")
+        st = attn.attn_fwd_bf16_partial(q.data_ptr(), k.data_ptr(), v.data_ptr(), o_part.data_ptr(),
+                                        lse_part.data_ptr(), B, H, H, Sq, Sk, total - Sk, total,
+                                        attn.LAYOUTS["bshd"], attn.MASKS[mask], s)
+        assert st == 0, attn.attn_fwd_bf16_strerror(st)
+        torch.cuda.synchronize()
+        if mask == "causal":
+            assert np.all(lse_part.cpu().numpy() == -np.inf)
+            assert np.all(o_part.cpu().numpy() == 0.0)
+        else:
+            o, lse = merge(o_part, lse_part, q, "bshd", "rtna")
+            o1, lse1 = torch.empty_like(q), torch.empty_like(lse)
+            launch_gqa(q, k, v, o1, "bshd", "rtna", "causal_br", lse=lse1)
+            torch.cuda.synchronize()
+            assert np.array_equal(to_bits(o), to_bits(o1))
+            assert np.array_equal(lse.cpu().numpy().view(np.uint32), lse1.cpu().numpy().view(np.uint32))
