@@ -160,7 +160,17 @@ struct Split {
   int tiles_per_split;
   float* part;
   float* ml;
+  // 0: the split items are work items n_whole, n_whole + 1, ... in order.
+  // Otherwise every item is split (n_whole = 0) and this is the number of
+  // (b, h) pairs: split item i is q-tile rank i / qt_major of pair
+  // i % qt_major, so the longest q-tiles of every head come first.
+  int qt_major;
 };
+
+// work item (b, h, q-tile rank) of split item i
+__device__ __forceinline__ int split_item_work(const Split& sp, int i, int n_qtiles) {
+  return sp.qt_major ? (i % sp.qt_major) * n_qtiles + i / sp.qt_major : sp.n_whole + i;
+}
 
 // Variable-length batches: sequence b holds the packed query rows
 // cu_q[b] .. cu_q[b+1]-1 and key rows cu_k[b] .. cu_k[b+1]-1 (offsets read on
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     work = xcd * per + (xcd < rem ? xcd : rem) + local;
   } else {
     slot = id - sp.n_whole;
-    work = sp.n_whole + slot / sp.splits;
+    work = split_item_work(sp, slot / sp.splits, n_qtiles);
     t_begin = (slot % sp.splits) * sp.tiles_per_split;
     t_end = t_begin + sp.tiles_per_split < t_end ? t_begin + sp.tiles_per_split : t_end;
   }
@@ -792,7 +802,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(uint16_t* __restrict__ 
   const int c4 = (int)(gid % (D / 4));
   const int row = (int)((gid / (D / 4)) % BM);
   const int item = (int)(gid / ((D / 4) * BM));
-  const int work = sp.n_whole + item;
+  const int work = split_item_work(sp, item, n_qtiles);
   const int qt = reverse_qt ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles, bh = work / n_qtiles;
   const int h = bh % H, b = bh / H;
   const int qrow = qt * BM + row;
@@ -914,6 +924,7 @@ bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
 constexpr int kMinSplitTiles = 4;
 struct Plan {
   int64_t n_whole, n_split_items, splits, tiles_per_split;
+  int64_t qt_major = 0;  // Split::qt_major
 };
 Plan make_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu) {
   Plan p{n_work, 0, 1, n_tiles};
@@ -940,17 +951,30 @@ int64_t causal_tiles(int64_t qt, int64_t Sq, int64_t Sk, int mask) {
   const int64_t hi = r_last + off < Sk - 1 ? r_last + off : Sk - 1;
   return hi < 0 ? 1 : hi / BN + 1;
 }
-// Split plan under a mask.  The items of a causal launch differ in length;
-// the last round is split only when they are nearly equal (the lightest
-// q-tile visits at least 3/4 of the tiles of the heaviest, as when Sq is
-// small against Sk with the bottom-right diagonal): otherwise the
-// longest-first item order already keeps the CUs busy to the end.  A split
-// item cuts its own visible tiles into `splits` ranges.
+// Split plan under a mask.  The items of a causal launch differ in length.
+// When they are nearly equal (the lightest q-tile visits at least 3/4 of the
+// tiles of the heaviest, as when Sq is small against Sk with the bottom-right
+// diagonal) only the partly idle last round is split, as without a mask.
+// When they are not, several rounds of items keep the CUs busy to the end in
+// the longest-first order, but one round or less does not: the longest item
+// alone sets the time, about twice the mean load.  Then every item is cut
+// into `splits` ranges of its own visible tiles, up to twice as many
+// workgroups as CUs (at most 8 ranges an item, each at least kMinSplitTiles
+// tiles of the longest item).
 Plan make_plan_masked(int64_t n_work, int64_t n_qtiles, int64_t Sq, int64_t Sk, int mask, int64_t n_cu) {
   if (mask == ATTN_MASK_NONE) return make_plan(n_work, (Sk + BN - 1) / BN, n_cu);
   const int64_t n_max = causal_tiles(n_qtiles - 1, Sq, Sk, mask), n_min = causal_tiles(0, Sq, Sk, mask);
-  if (4 * n_min < 3 * n_max) return Plan{n_work, 0, 1, n_max};
-  return make_plan(n_work, n_max, n_cu);
+  if (4 * n_min >= 3 * n_max) return make_plan(n_work, n_max, n_cu);
+  const Plan whole{n_work, 0, 1, n_max};
+  if (n_cu < 1 || n_work > n_cu) return whole;
+  int64_t splits = 2 * n_cu / n_work;
+  if (splits > 8) splits = 8;
+  if (splits > n_max / kMinSplitTiles) splits = n_max / kMinSplitTiles;
+  if (splits < 2) return whole;
+  // all items split, dispatched longest q-tile first across the heads (the
+  // ranges of one q-tile rank are nearly equal): in head order the longest
+  // items of the last heads would start last
+  return Plan{0, n_work, splits, (n_max + splits - 1) / splits, n_work / n_qtiles};
 }
 int64_t plan_workspace_bytes(const Plan& p) {
   return p.n_split_items * p.splits * BM * (D + 2) * (int64_t)sizeof(float);
@@ -1042,7 +1066,7 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
         int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream,
         const Varlen* vl = nullptr, float* lse = nullptr) {
   const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
-  Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr};
+  Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr, (int)plan.qt_major};
   if (plan.n_split_items > 0) {
     sp.part = (float*)workspace;
     sp.ml = sp.part + plan.n_split_items * plan.splits * BM * D;
@@ -1190,7 +1214,7 @@ extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v
   const int64_t off_global = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT ? Sk_total - Sq : 0;
   const int64_t off = off_global - key_offset;
   const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
-  const Split sp{(int)pb.n_work, 1, (int)pb.n_tiles, nullptr, nullptr};
+  const Split sp{(int)pb.n_work, 1, (int)pb.n_tiles, nullptr, nullptr, 0};
   const Varlen none{nullptr, nullptr, 0, 0, 0};
   const dim3 grid((unsigned)pb.n_work), block(NTHREADS);
   const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;

@@ -254,6 +254,8 @@ WORKLOADS = {
     "prefill_br": Workload("prefill_br", 2, 24, 4097, 32771, "bshd", ("rtz",), mask="causal_br"),
     # grouped-query causal prefill: 32 query heads over 8 K/V heads
     "gqa8k_causal": Workload("gqa8k_causal", 2, 32, 8192, 8192, "bshd", ("rtne",), mask="causal", H_kv=8),
+    # one long causal sequence over few heads: 256 work items of 4 .. 256 key tiles, a single round
+    "causal16k_4h": Workload("causal16k_4h", 1, 4, 16384, 16384, "bshd", ("rtne",), mask="causal"),
 }
 
 

@@ -244,14 +244,17 @@ int attn_fwd_bf16_varlen(const void *q, const void *k, const void *v, void *o,
  * as attn_fwd_bf16_ws does for the unmasked call.
  *
  * Without a mask the split is attn_fwd_bf16_ws's.  Under a causal mask the
- * work items (256 query rows of one head) see different numbers of keys; the
- * last, partly filled round of compute units is split only when the items
- * are nearly equal (the first q-tile of a head sees at least 3/4 of the key
- * tiles of its last: a short Sq against a long Sk with the bottom-right
- * diagonal, the shape of a prefill after cached keys), and a split item cuts
- * the key tiles its rows see into equal consecutive ranges.  Otherwise the
- * call runs single-pass (longest items first).  With lse, the rows of split
- * items get the log-sum-exp of the merged sums.
+ * work items (256 query rows of one head) see different numbers of keys, and
+ * a split item cuts the key tiles its rows see into equal consecutive
+ * ranges.  When the items are nearly equal (the first q-tile of a head sees
+ * at least 3/4 of the key tiles of its last: a short Sq against a long Sk
+ * with the bottom-right diagonal, the shape of a prefill after cached keys)
+ * the last, partly filled round of compute units is split.  When they are
+ * not and all of them fit in one round (few heads of a long sequence), every
+ * item is split into up to 8 ranges, for up to twice as many workgroups as
+ * compute units: the longest item would otherwise set the time alone.
+ * Otherwise the call runs single-pass (longest items first).  With lse, the
+ * rows of split items get the log-sum-exp of the merged sums.
  *
  *   workspace       : at least attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk,
  *                     mask) bytes, 16-byte aligned, not overlapping q, k, v,
@@ -274,8 +277,8 @@ int attn_fwd_bf16_gqa_ws(const void *q, const void *k, const void *v, void *o,
  * attn_fwd_bf16_gqa_workspace_size -- bytes of workspace attn_fwd_bf16_gqa_ws
  * needs for this shape and mask on the current device (0: it will not
  * split; the K/V head count does not matter).  Returns ATTN_ERR_NULL,
- * ATTN_ERR_SIZE, ATTN_ERR_MASK or ATTN_ERR_DEVICE.  Bounded like
- * attn_fwd_bf16_workspace_size's.
+ * ATTN_ERR_SIZE, ATTN_ERR_MASK or ATTN_ERR_DEVICE.  At most 2 x 256 (compute
+ * units) partial blocks of 256 rows x 130 floats.
  */
 int attn_fwd_bf16_gqa_workspace_size(int64_t B, int64_t H, int64_t Sq, int64_t Sk,
                                      int mask, int64_t *bytes);

@@ -310,6 +310,10 @@ def test_masked_plan_without_mask_is_the_plain_plan(n_heads, Sq, Sk):
     (24, 512, 1280, "causal_br", (0, 48, 5, 4)),        # q-tiles see 16 and 20 tiles: 5 ranges of the longest
     (4, 300, 2000, "causal_br", (0, 8, 8, 4)),
     (4, 2000, 300, "causal_br", (32, 0, 1, 5)),         # Sq > Sk: the first q-tiles see no key
+    (4, 16384, 16384, "causal", (0, 256, 2, 128)),      # one round of unequal items (4 .. 256 tiles): all cut in 2
+    (2, 8192, 8192, "causal", (0, 64, 8, 16)),          # 64 items: 8 ranges each
+    (1, 1000, 1000, "causal", (0, 4, 4, 4)),            # ranges of at least 4 tiles of the longest item
+    (16, 8192, 8192, "causal", (512, 0, 1, 128)),       # two rounds: longest first, no split
 ])
 def test_masked_plan_cases(n_heads, Sq, Sk, mask, expect):
     assert _masked_plan(n_heads, Sq, Sk, mask) == expect
@@ -324,13 +328,20 @@ def test_masked_plan_invariants(mask, n_heads, Sq, Sk):
     n_qt = -(-Sq // 256)
     whole, items, splits, tps = _masked_plan(n_heads, Sq, Sk, mask, n_cu)
     tiles = [_causal_tiles(qt, Sq, Sk, mask) for qt in range(n_qt)]
-    assert whole + items == n_heads * n_qt
+    n_work = n_heads * n_qt
+    assert whole + items == n_work
     if items == 0:
         assert splits == 1
+        # nothing split: nearly equal items filling whole rounds, unequal ones over several
+        # rounds, or too few tiles to cut
+        assert (4 * min(tiles) >= 3 * max(tiles)) or n_work > n_cu or max(tiles) < 8
         return
-    assert 4 * min(tiles) >= 3 * max(tiles)  # split only when the items are nearly equal
-    assert whole % n_cu == 0 and 0 < items < n_cu and items * splits <= n_cu
     assert splits >= 2 and tps >= 4 and (splits - 1) * tps < max(tiles) <= splits * tps
+    if 4 * min(tiles) >= 3 * max(tiles):  # nearly equal items: only the partly idle last round
+        assert whole % n_cu == 0 and 0 < items < n_cu and items * splits <= n_cu
+    else:  # unequal items in one round: all of them, up to twice as many workgroups as CUs
+        assert n_work <= n_cu and whole == 0 and items == n_work
+        assert splits <= 8 and n_work * splits <= 2 * n_cu
 
 
 def test_masked_plan_argument_errors():

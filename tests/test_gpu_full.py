@@ -152,6 +152,12 @@ def test_causal_bottom_right_prefill_odd_lengths():
 
 
 @pytest.mark.timeout(600)
+def test_causal_long_sequence_few_heads():
+    # B=1 H=4 Sq=Sk=16384 BSHD RTNE, causal: one round of unequal items, all cut into key ranges
+    _run_config("causal16k_4h")
+
+
+@pytest.mark.timeout(600)
 def test_grouped_query_causal_8k():
     # B=2 H=32 H_kv=8 Sq=Sk=8192 BSHD RTNE, causal: query head h uses K/V head h / 4
     _run_config("gqa8k_causal")

@@ -5,7 +5,8 @@ Under a causal mask a work item (256 query rows of one head) visits the key
 tiles up to its last row's limit.  When the items are nearly equal (a short
 Sq against a long Sk, diagonal at the bottom right) and do not fill the last
 round of compute units, each item of that round cuts its visible tiles into
-consecutive ranges and a second kernel merges the partial rows.  Every row is
+consecutive ranges and a second kernel merges the partial rows; when they
+are unequal and all fit in one round, every item is cut.  Every row is
 checked against the fp64 oracle under the row-scaled 2-ULP gate in every
 rounding mode, the lse within its fp32 bound, and repeated calls for
 identical bits; items that run whole must give exactly the single-pass bits.
@@ -58,6 +59,10 @@ SHAPES = [
     (1, 8, 2, 300, 2000, "causal_br"),   # grouped K/V heads
     (2, 4, 1, 300, 2000, "none"),        # multi-query heads, no mask
     (1, 3, 3, 1000, 7000, "causal_br"),  # ragged last q-tile (232 rows)
+    # one round of unequal items (top-left diagonal, few heads): every item cut into ranges
+    (1, 2, 2, 1000, 1000, "causal"),     # 8 items of 4 .. 16 tiles, 4 ranges each (some empty)
+    (1, 3, 1, 777, 2500, "causal"),      # 12 items of 4 .. 13 tiles, 3 ranges each
+    (2, 2, 1, 1500, 1500, "causal_br"),  # Sq = Sk: the bottom-right diagonal is the top-left one
 ]
 
 
@@ -118,12 +123,13 @@ def test_whole_items_keep_the_single_pass_bits():
     assert res.ok, res.summary()
 
 
-@pytest.mark.parametrize("shape", [(1, 4, 4, 700, 700, "causal"), (2, 4, 2, 300, 2000, "causal"),
+@pytest.mark.parametrize("shape", [(1, 96, 96, 700, 700, "causal"), (2, 4, 2, 300, 2000, "causal"),
                                    (1, 4, 4, 2000, 300, "causal_br")], ids=lambda s: "x".join(map(str, s[:5])) + s[5])
 def test_unequal_items_run_single_pass(shape):
-    # top-left diagonal (or Sq > Sk at the bottom right): the q-tiles of a head
-    # see very different key counts, so nothing is split and the call is
-    # attn_fwd_bf16_gqa exactly
+    # the q-tiles of a head see very different key counts: over more than one
+    # round of items (288 here) the longest-first order keeps the CUs busy, and
+    # items of at most 7 tiles are too short to cut, so nothing is split and the
+    # call is attn_fwd_bf16_gqa exactly
     B, H, H_kv, Sq, Sk, mask = shape
     assert attn.attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, attn.MASKS[mask]) == 0
     inp = synth.small(B, H, Sq, Sk, "bhsd", seed=3, mask=mask, H_kv=H_kv)
