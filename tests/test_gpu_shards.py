@@ -226,3 +226,35 @@ def test_shards_far_along_a_long_sequence():
             torch.cuda.synchronize()
             assert np.array_equal(to_bits(o), to_bits(o1))
             assert np.array_equal(lse.cpu().numpy().view(np.uint32), lse1.cpu().numpy().view(np.uint32))
+
+
+def test_partial_and_merge_write_only_their_rows():
+    B, H, Sq, Sk, cuts = 1, 2, 300, 700, [0, 300, 700]
+    inp = synth.small(B, H, Sq, Sk, "bhsd", seed=62)
+    q, k, v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+    pad, n_rows = 4096, B * H * Sq
+    n_part = q.numel()
+    p_buf = torch.full((2 * n_part + 2 * pad,), -777.0, dtype=torch.float32, device="cuda:0")
+    l_buf = torch.full((2 * n_rows + 2 * pad,), -777.0, dtype=torch.float32, device="cuda:0")
+    o_parts = p_buf[pad:pad + 2 * n_part].view((2,) + tuple(q.shape))
+    lse_parts = l_buf[pad:pad + 2 * n_rows].view(2, B, H, Sq)
+    s = torch.cuda.current_stream().cuda_stream
+    for i in range(2):
+        ks, vs = _shard(k, "bhsd", cuts[i], cuts[i + 1]), _shard(v, "bhsd", cuts[i], cuts[i + 1])
+        assert attn.attn_fwd_bf16_partial(q.data_ptr(), ks.data_ptr(), vs.data_ptr(), o_parts[i].data_ptr(),
+                                          lse_parts[i].data_ptr(), B, H, H, Sq, cuts[i + 1] - cuts[i], cuts[i], Sk,
+                                          attn.LAYOUTS["bhsd"], attn.MASKS["none"], s) == 0
+        torch.cuda.synchronize()
+    o_buf = torch.full((q.numel() + 2 * pad,), 0x7E7E, dtype=torch.int16, device="cuda:0")
+    m_buf = torch.full((n_rows + 2 * pad,), -777.0, dtype=torch.float32, device="cuda:0")
+    o = o_buf[pad:pad + q.numel()]
+    lse = m_buf[pad:pad + n_rows]
+    assert attn.attn_fwd_bf16_merge(o_parts.data_ptr(), lse_parts.data_ptr(), 2, o.data_ptr(), lse.data_ptr(), B, H,
+                                    Sq, attn.LAYOUTS["bhsd"], attn.ROUND_MODES["rtz"], s) == 0
+    torch.cuda.synchronize()
+    for buf, n, fill in ((p_buf, 2 * n_part, -777.0), (l_buf, 2 * n_rows, -777.0), (m_buf, n_rows, -777.0)):
+        a = buf.cpu().numpy()
+        assert np.all(a[:pad] == fill) and np.all(a[pad + n:] == fill)
+        assert not np.any(a[pad:pad + n] == fill)  # every element inside was written
+    ob = o_buf.cpu().numpy()
+    assert np.all(ob[:pad] == 0x7E7E) and np.all(ob[pad + q.numel():] == 0x7E7E)

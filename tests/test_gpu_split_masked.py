@@ -170,3 +170,22 @@ def test_workspace_errors_on_device():
     assert attn.attn_fwd_bf16_gqa_ws(*args, o.data_ptr(), need, s) == 6       # ATTN_ERR_ALIAS
     assert attn.attn_fwd_bf16_gqa_ws(*args, ws.data_ptr(), need, s) == 0
     torch.cuda.synchronize()
+
+
+def test_split_writes_stay_inside_o_and_lse():
+    # o and lse carved out of larger buffers filled with sentinels: the split kernel, the merge and
+    # the lse stores touch nothing outside them (the ragged last q-tile's rows >= Sq included)
+    B, H, Sq, Sk, mask = 1, 4, 300, 2000, "causal_br"
+    inp = synth.small(B, H, Sq, Sk, "bshd", seed=61, mask=mask)
+    q, k, v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+    pad = 4096  # elements on each side
+    n_o, n_l = q.numel(), B * H * Sq
+    o_buf = torch.full((n_o + 2 * pad,), 0x7E7E, dtype=torch.int16, device="cuda:0")
+    l_buf = torch.full((n_l + 2 * pad,), -12345.0, dtype=torch.float32, device="cuda:0")
+    o = o_buf[pad:pad + n_o].view(torch.bfloat16).view(q.shape)
+    lse = l_buf[pad:pad + n_l].view(B, H, Sq)
+    assert launch_gqa_ws(q, k, v, o, "bshd", "rtne", mask, lse=lse) > 0
+    ob, lb = o_buf.cpu().numpy(), l_buf.cpu().numpy()
+    assert np.all(ob[:pad] == 0x7E7E) and np.all(ob[pad + n_o:] == 0x7E7E)
+    assert np.all(lb[:pad] == -12345.0) and np.all(lb[pad + n_l:] == -12345.0)
+    assert np.all(np.isfinite(lb[pad:pad + n_l]))
