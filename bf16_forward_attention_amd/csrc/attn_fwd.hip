@@ -644,6 +644,8 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     mx = m;
   };
 
+  // a wave whose 32 rows all lie past Sq (the ragged last q-tile) skips the products
+  const bool idle = __builtin_amdgcn_readfirstlane(qt * BM + wave * 32) >= Sq;
   // ---- main loop: four LDS stages, tiles loaded three ahead, one barrier per tile ----
   // Tile t lives in stage t % 4.  Iteration t turns the logits of tile t
   // (S[t%2]) into weights while the matrix core computes the logits of tile
@@ -656,6 +658,20 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   // tile t+3.
   auto body = [&](auto st_c, auto masked_c, int t) __attribute__((always_inline)) {
     constexpr int ST = decltype(st_c)::value, P = ST & 1;
+    if (idle) {
+      // no valid row in this wave: only its share of the tile loads and the barrier
+      __builtin_amdgcn_s_waitcnt(0x0F74);
+      __syncthreads();
+      i32x4 rk, rv;
+      tile_rsrc(t + 3, rk, rv);
+      uint32_t lw = lds_wave;
+      asm volatile("" : "+s"(lw));
+      dma_k(rk, lw, (ST + 3) % NSTAGE, 0);
+      dma_k(rk, lw, (ST + 3) % NSTAGE, 1);
+      dma_v(rv, lw, (ST + 3) % NSTAGE, 0);
+      dma_v(rv, lw, (ST + 3) % NSTAGE, 1);
+      return;
+    }
     rescale();
     __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4): only the loads of tile t+2 may still be in flight
     __syncthreads();
