@@ -646,6 +646,13 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
 
   // a wave whose 32 rows all lie past Sq (the ragged last q-tile) skips the products
   const bool idle = __builtin_amdgcn_readfirstlane(qt * BM + wave * 32) >= Sq;
+  // CAUSAL: the last key tile this wave's rows see (its last valid row's limit; -1: none)
+  int wave_last_tile = 0;
+  if constexpr (CAUSAL) {
+    const int64_t r_w = (int64_t)qt * BM + wave * 32 + 31 < Sq ? (int64_t)qt * BM + wave * 32 + 31 : (int64_t)Sq - 1;
+    const int64_t lim_w = r_w + causal_off < (int64_t)Sk - 1 ? r_w + causal_off : (int64_t)Sk - 1;
+    wave_last_tile = __builtin_amdgcn_readfirstlane(lim_w < 0 ? -1 : (int)(lim_w / BN));
+  }
   // ---- main loop: four LDS stages, tiles loaded three ahead, one barrier per tile ----
   // Tile t lives in stage t % 4.  Iteration t turns the logits of tile t
   // (S[t%2]) into weights while the matrix core computes the logits of tile
@@ -724,15 +731,32 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
       body(S3{}, Plain{}, t + 3);
       t += 4;
     }
-    while (t < n_tiles) {
+    // Past the last tile its own rows see, a wave's weights are exact zeros
+    // and its row maxima -Inf: it leaves the products there and only issues
+    // its share of the remaining tile loads, meeting the barrier each tile.
+    const int n_w = wave_last_tile - t_begin + 1 < n_tiles ? wave_last_tile - t_begin + 1 : n_tiles;
+    while (t < n_w) {
       body(S0{}, Masked{}, t);
-      if (++t == n_tiles) break;
+      if (++t == n_w) break;
       body(S1{}, Masked{}, t);
-      if (++t == n_tiles) break;
+      if (++t == n_w) break;
       body(S2{}, Masked{}, t);
-      if (++t == n_tiles) break;
+      if (++t == n_w) break;
       body(S3{}, Masked{}, t);
       ++t;
+    }
+    for (; t < n_tiles; ++t) {
+      __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+      __syncthreads();
+      i32x4 rk, rv;
+      tile_rsrc(t + 3, rk, rv);
+      const int st = (t + 3) % NSTAGE;
+      uint32_t lw = lds_wave;
+      asm volatile("" : "+s"(lw));
+      dma_k(rk, lw, st, 0);
+      dma_k(rk, lw, st, 1);
+      dma_v(rv, lw, st, 0);
+      dma_v(rv, lw, st, 1);
     }
   } else {
     // (written as an exit test after each body: a test before the first one
