@@ -255,9 +255,12 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // 0 .. up to its last row's limit in order (so the q-tiles of a head stream
 // the same tiles together, as without a mask): those every row sees whole in
 // a loop without mask code, then the diagonal ones (some row's limit falls
-// inside or before them) with the mask applied beside the row maxima.  With
-// SPLIT, a split item's visible tiles are cut into sp.splits ranges of equal
-// length (the last ones may be shorter or empty).
+// inside or before them) with the mask applied beside the row maxima; a wave
+// past the last tile its own rows see only loads and meets the barriers.
+// With SPLIT, a split item's visible tiles are cut into sp.splits ranges of
+// equal length (the last ones may be shorter or empty).
+// In every instantiation a wave whose 32 rows all lie past Sq (the ragged
+// last q-tile) skips the products and only loads.
 template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
 __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
