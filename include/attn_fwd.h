@@ -97,8 +97,10 @@ typedef enum {
  * O is valid after the stream reaches that point.  Argument errors
  * (ATTN_ERR_NULL .. ATTN_ERR_ALIAS) are detected before any HIP call and
  * nothing is launched.  ATTN_ERR_DEVICE: the current device is not gfx950.
- * ATTN_ERR_HIP: the launch was rejected.  Faults inside the kernel surface at
- * the caller's next synchronisation, as for any HIP kernel.
+ * ATTN_ERR_HIP: the launch was rejected (read with hipGetLastError right after
+ * the launches, so an earlier error of the calling thread that nobody read is
+ * reported here too, and cleared).  Faults inside the kernel surface at the
+ * caller's next synchronisation, as for any HIP kernel.
  */
 int attn_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                   int64_t B, int64_t H, int64_t Sq, int64_t Sk,
