@@ -1,0 +1,74 @@
+"""bench.py's host logic, without a GPU: the FLOP count of each workload (the
+visible (query, key) pairs against a brute-force count), the code hash that
+ties the committed traffic counters to a kernel version, the traffic reader,
+and the refusal of more than one GPU."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import bench
+from bf16_forward_attention_amd import synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _pairs_brute(Sq, Sk, mask):
+    i = np.arange(Sq)[:, None]
+    j = np.arange(Sk)[None, :]
+    if mask == "none":
+        return Sq * Sk
+    off = 0 if mask == "causal" else Sk - Sq
+    return int(np.sum(j <= i + off))
+
+
+@pytest.mark.parametrize("mask", ["none", "causal", "causal_br"])
+@pytest.mark.parametrize("Sq,Sk", [(1, 1), (7, 300), (300, 7), (257, 257), (1000, 64), (64, 1000)])
+def test_workload_flops_counts_visible_pairs(mask, Sq, Sk):
+    wl = synth.Workload("t", 2, 3, Sq, Sk, "bshd", ("rtne",), mask=mask)
+    assert bench.workload_flops(wl) == 4 * 128 * 2 * 3 * _pairs_brute(Sq, Sk, mask)
+
+
+def test_named_workloads_flops():
+    assert bench.workload_flops(synth.WORKLOADS["self8k"]) == 4 * 128 * 4 * 16 * 8192 * 8192
+    # causal at Sq = Sk: S(S+1)/2 pairs per head
+    assert bench.workload_flops(synth.WORKLOADS["self8k_causal"]) == 4 * 128 * 4 * 16 * 8192 * 8193 // 2
+    wl = synth.WORKLOADS["prefill_br"]
+    assert bench.workload_flops(wl) == 4 * 128 * wl.B * wl.H * _pairs_brute(wl.Sq, wl.Sk, "causal_br")
+
+
+def test_varlen_pairs_match_a_brute_force_count():
+    wl = synth.VARLEN_WORKLOADS["varlen_mix"]
+    got = bench.varlen_visible_pairs(wl)
+    expect = [_pairs_brute(sq, sk, wl.mask) for sq, sk in zip(wl.lengths_q, wl.lengths_k)]
+    assert got.tolist() == expect and sum(wl.lengths_q) == 77048
+
+
+def test_code_hash_ignores_comments_and_follows_code(tmp_path, monkeypatch):
+    src = os.path.join(ROOT, "bf16_forward_attention_amd", "csrc", "attn_fwd.hip")
+    text = open(src).read()
+    base = bench.kernel_code_sha256()
+    fake_root = tmp_path / "r"
+    (fake_root / "bf16_forward_attention_amd" / "csrc").mkdir(parents=True)
+    dst = fake_root / "bf16_forward_attention_amd" / "csrc" / "attn_fwd.hip"
+    monkeypatch.setattr(bench, "ROOT", str(fake_root))
+    dst.write_text("// a new comment line\n\n" + text.replace("constexpr int BM = 256;", "constexpr int BM = 256;  // rows"))
+    assert bench.kernel_code_sha256() == base
+    dst.write_text(text.replace("constexpr int BM = 256;", "constexpr int BM = 128;"))
+    assert bench.kernel_code_sha256() != base
+
+
+def test_traffic_summary_is_used_only_for_its_kernel(monkeypatch):
+    got = bench.measured_traffic("self8k")
+    assert got is not None and abs(got - 536_870_912 * 1.0005) < 0.01 * 536_870_912  # Q+K+V+O once
+    monkeypatch.setattr(bench, "kernel_code_sha256", lambda: "0" * 64)
+    assert bench.measured_traffic("self8k") is None
+    assert bench.measured_traffic("no_such_workload") is None
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 2 and "one GPU" in (r.stdout + r.stderr)
