@@ -23,7 +23,7 @@ from tests.gpu_util import MODES, launch_gqa, launch_gqa_ws, say, to_bits, to_de
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 36
+N_CASES = 120
 
 
 def _draw(i):
@@ -113,3 +113,56 @@ def test_random_case(i):
     torch.cuda.synchronize()
     res = gate(logical(o3), rdm, ex)
     assert res.ok, f"shards {cuts}: {res.summary()}"
+
+
+@pytest.mark.parametrize("i", range(40))
+def test_random_varlen_case(i):
+    # packed sequences of random lengths (some without queries or without keys), grouped heads,
+    # a random mask and mode, through attn_fwd_bf16_varlen with lse
+    rng = np.random.default_rng(9000 + i)
+    nseq = int(rng.integers(1, 7))
+    lq = [int(x) for x in rng.choice([0, 1, 5, 64, 65, 200, 256, 257, 600], size=nseq)]
+    lk = [int(x) for x in rng.choice([0, 1, 7, 64, 100, 300, 513, 900], size=nseq)]
+    if sum(lq) == 0:
+        lq[0] = 3
+    if sum(lk) == 0:
+        lk[-1] = 5
+    H_kv = int(rng.choice([1, 2]))
+    H = H_kv * int(rng.choice([1, 3]))
+    mode = MODES[rng.integers(3)]
+    mask = ["none", "causal", "causal_br"][rng.integers(3)]
+    say(f"  varlen case {i}: lq={lq} lk={lk} H={H} H_kv={H_kv} {mode} {mask}")
+    wl = synth.VarlenWorkload(f"rv{i}", tuple(lq), tuple(lk), H, H_kv, (mode,), mask=mask, seed=300 + i)
+    inp = synth.generate_varlen(wl)
+    rows = [(t, h) for t in range(sum(lq)) for h in range(H)]
+    ex, rd, ref_lse = oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows, mask=mask,
+                                              with_lse=True)
+    q = torch.from_numpy(inp.q.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    k = torch.from_numpy(inp.k.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    v = torch.from_numpy(inp.v.view(np.int16)).view(torch.bfloat16).to("cuda:0")
+    cq = torch.from_numpy(inp.cu_q).to("cuda:0")
+    ck = torch.from_numpy(inp.cu_k).to("cuda:0")
+    out, lse = attn.attn_fwd_varlen(q, k, v, cq, ck, max(lq), round_mode=mode, mask=mask, with_lse=True)
+    torch.cuda.synchronize()
+    got = to_bits(out).reshape(-1, 128)
+    res = gate(got, rd[:, MODES.index(mode)], ex)
+    assert res.ok, res.summary()
+    got_lse = lse.cpu().numpy().T.reshape(-1)  # [H, total_q] -> rows (t, h)
+    # the derived fp32 bound, from each row's own sequence: largest |q|.|k| over its visible keys
+    dmax = np.zeros(len(rows))
+    nvis = np.zeros(len(rows))
+    for b in range(nseq):
+        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        if q1 == q0:
+            continue
+        qa = np.abs(cases.val(inp.q[q0:q1]))                                   # [Sq, H, 128]
+        ka = np.repeat(np.abs(cases.val(inp.k[k0:k1])), H // H_kv, axis=1)   # [Sk, H, 128]
+        dots = np.einsum("ihd,jhd->ihj", qa, ka) / math.sqrt(128)
+        Sq_b, Sk_b = q1 - q0, k1 - k0
+        ii, jj = np.arange(Sq_b)[:, None], np.arange(Sk_b)[None, :]
+        vis = np.ones((Sq_b, Sk_b), bool) if mask == "none" else jj <= ii + (0 if mask == "causal" else Sk_b - Sq_b)
+        d = np.where(vis[:, None, :], dots, 0.0)
+        dmax[q0 * H:q1 * H] = d.max(axis=-1, initial=0.0).reshape(-1)
+        nvis[q0 * H:q1 * H] = np.repeat(vis.sum(axis=-1), H)
+    ok, worst, _ = lse_gate(got_lse, ref_lse, lse_tolerance(dmax, nvis, ref_lse))
+    assert ok, f"lse worst err/tol {worst:.3f}"
