@@ -15,8 +15,8 @@ BSHD, RTNE.  Prints one JSON line:
              per-launch duration measured by HIP events on the launch stream
   cpu_baseline  the fp64 oracle on a bounded sample of the same workload's
              rows, timed on this host's cores (a reported baseline only)
-  parity     the same sampled rows of the timed output checked against the
-             oracle under the row-scaled 2-ULP gate
+  parity     rows of the timed output, taken from those the CPU baseline
+             computed, checked against them under the row-scaled 2-ULP gate
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S]
@@ -61,15 +61,6 @@ def parse():
     return p.parse_args()
 
 
-def sample_rows(wl, n, stream):
-    """``n`` seeded distinct (b, h, i) rows of the workload, sorted by head."""
-    from bf16_forward_attention_amd import synth
-
-    total = wl.B * wl.H * wl.Sq
-    flat = synth.floyd_sample(wl.seed, synth.TID_SUBSET, total, min(n, total), stream=stream)
-    return [(f // (wl.H * wl.Sq), (f // wl.Sq) % wl.H, f % wl.Sq) for f in flat]
-
-
 def head_rows(wl, n, b, h, stream):
     """``n`` seeded distinct query rows of head (b, h)."""
     from bf16_forward_attention_amd import synth
@@ -91,11 +82,14 @@ def workload_flops(wl) -> float:
     return 4.0 * 128 * wl.B * wl.H * float(visible_keys(wl, np.arange(wl.Sq)).sum())
 
 
-def cpu_baseline(inp, target_s):
+def cpu_baseline(inp, target_s, n_parity):
     """Time the oracle, as it stands, on a bounded row sample of this workload.
 
     A short probe (rows of one head) sizes the sample to about ``target_s``
-    seconds; the timed sample then takes rows from consecutive heads.
+    seconds; the timed sample then takes rows from consecutive heads.  Returns
+    the baseline record and, for the parity check of the GPU output, up to
+    ``n_parity`` of the timed rows (evenly spread) with the oracle's outputs
+    for them: the oracle runs only here.
     """
     import oracle
 
@@ -122,14 +116,16 @@ def cpu_baseline(inp, target_s):
         rows += head_rows(wl, take, bh // wl.H, bh % wl.H, stream=(1 << 21) + bh)
         bh += 1
     t0 = time.perf_counter()
-    oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, threads, mask=wl.mask)
+    ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, threads, mask=wl.mask)
     dt = time.perf_counter() - t0
     pairs = int(visible_keys(wl, [i for _, _, i in rows]).sum())
     flops = 4.0 * pairs * 128
     keys = f"all {wl.Sk} keys each" if wl.mask == "none" else f"{pairs} visible (query, key) pairs"
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{len(rows)} seeded query rows from {bh} heads of {wl.name} ({keys}, "
-                      f"fp64 with 3 roundings), {dt:.2f} s"}
+    record = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+              "sample": f"{len(rows)} seeded query rows from {bh} heads of {wl.name} ({keys}, "
+                        f"fp64 with 3 roundings), {dt:.2f} s"}
+    idx = np.unique(np.linspace(0, len(rows) - 1, min(n_parity, len(rows))).astype(np.int64))
+    return record, [rows[i] for i in idx], ex[idx], rd[idx]
 
 
 def kernel_code_sha256() -> str:
@@ -301,13 +297,11 @@ def main():
                      "launch_ms_median": round(float(np.median(per)), 4)},
     }
     if not args.no_cpu_baseline:
-        import oracle
         from tests.gate import gate
 
         log("[bench] cpu baseline (oracle)")
-        result["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
-        rows = sample_rows(wl, args.parity_rows, stream=(1 << 20) + 2)
-        ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask=wl.mask)
+        result["cpu_baseline"], rows, ex, rd = cpu_baseline(inp, args.cpu_seconds, args.parity_rows)
+        # parity: the timed output on rows the baseline computed
         logical = synth.to_logical(out_bits, wl.layout)
         got = np.stack([logical[b, h, i] for b, h, i in rows])
         res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)
@@ -399,24 +393,18 @@ def main_varlen(args):
         import oracle
         from tests.gate import gate
 
-        total_q = q.shape[0]
-        flat = synth.floyd_sample(wl.seed, synth.TID_SUBSET, total_q * wl.H, min(args.parity_rows, total_q * wl.H),
-                                  stream=(1 << 20) + 2)
-        rows = [(f // wl.H, f % wl.H) for f in flat]
-        ex, rd = oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows, wl.mask)
-        got = np.stack([out_bits[t_, h] for t_, h in rows])
-        res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)
-        result["parity"] = {"rows": len(rows), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
-                            "strict_ulp_hist": res.strict_hist}
-        log(f"[bench] parity {res.summary()}")
-        # CPU baseline: the oracle on whole sequences' rows of one head, sized to about --cpu-seconds
+        # CPU baseline: the oracle on every query row of one head per sequence (head b mod H),
+        # sequence after sequence until about --cpu-seconds; the parity check then compares the
+        # timed output with rows of that sample (the oracle runs only here)
         threads = oracle.default_threads()
         sample, pairs, t0 = [], 0, time.perf_counter()
         seq_pairs = varlen_visible_pairs(wl)
         budget = args.cpu_seconds
+        done = []
         for b in range(wl.B):
-            rows_b = [(int(tq), 0) for tq in range(inp.cu_q[b], inp.cu_q[b + 1])]
-            oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows_b, wl.mask, threads)
+            rows_b = [(int(tq), b % wl.H) for tq in range(inp.cu_q[b], inp.cu_q[b + 1])]
+            ex_b, rd_b = oracle.attn_rows_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, rows_b, wl.mask, threads)
+            done.append((rows_b, ex_b, rd_b))
             sample.append(b)
             pairs += int(seq_pairs[b])
             if time.perf_counter() - t0 > budget:
@@ -424,8 +412,18 @@ def main_varlen(args):
         dt = time.perf_counter() - t0
         result["cpu_baseline"] = {"value": 4.0 * 128 * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": threads,
                                   "kind": "oracle",
-                                  "sample": f"every query row of head 0 of sequences {sample[0]}..{sample[-1]} of "
-                                            f"{wl.name} ({pairs} visible pairs, fp64 with 3 roundings), {dt:.2f} s"}
+                                  "sample": f"every query row of one head (b mod {wl.H}) of sequences {sample[0]}.."
+                                            f"{sample[-1]} of {wl.name} ({pairs} visible pairs, fp64 with 3 "
+                                            f"roundings), {dt:.2f} s"}
+        rows = [r for rb, _, _ in done for r in rb]
+        ex = np.concatenate([e for _, e, _ in done])
+        rd = np.concatenate([r_ for _, _, r_ in done])
+        idx = np.unique(np.linspace(0, len(rows) - 1, min(args.parity_rows, len(rows))).astype(np.int64))
+        got = np.stack([out_bits[rows[i][0], rows[i][1]] for i in idx])
+        res = gate(got, rd[idx, ("rtne", "rtna", "rtz").index(mode)], ex[idx])
+        result["parity"] = {"rows": len(idx), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
+                            "strict_ulp_hist": res.strict_hist}
+        log(f"[bench] parity {res.summary()}")
     print(json.dumps(result), flush=True)
 
 
