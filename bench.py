@@ -17,6 +17,10 @@ BSHD, RTNE.  Prints one JSON line:
              rows, timed on this host's cores (a reported baseline only)
   parity     rows of the timed output, taken from those the CPU baseline
              computed, checked against them under the row-scaled 2-ULP gate
+  clock      the shader clock of each XCD and the socket power (amd-smi) during
+             about 4 s more of the same launches right after the timed region, and
+             the rate over the last 2 s of them (sustained_tflops)
+  env        ROCm and torch versions, the device, the hipcc flags of the build
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S]
@@ -26,6 +30,8 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import shutil
+import subprocess
 import sys
 import time
 
@@ -42,6 +48,127 @@ PEAK_BF16_TFLOPS = 256 * 2.4e9 * 4096 / 1e12
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
+
+
+def amd_smi(*args):
+    """One ``amd-smi ... --json`` query, parsed; None where the tool is missing or fails."""
+    exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
+    try:
+        out = subprocess.run([exe, *args, "--json"], capture_output=True, text=True, timeout=20).stdout
+        starts = [i for i in (out.find("{"), out.find("[")) if i >= 0]
+        return json.JSONDecoder().raw_decode(out[min(starts):])[0] if starts else None
+    except (OSError, subprocess.SubprocessError, ValueError):
+        return None
+
+
+def _gpu_entries(obj):
+    if isinstance(obj, dict):
+        obj = obj.get("gpu_data", [obj])
+    return [g for g in obj if isinstance(g, dict)] if isinstance(obj, list) else []
+
+
+def smi_index(bdf: str, listing) -> int | None:
+    """amd-smi's index of the GPU at PCI address ``bdf`` ("dddd:bb:dd"), from ``amd-smi list``."""
+    for g in _gpu_entries(listing):
+        if str(g.get("bdf", "")).lower().startswith(bdf.lower()) and "gpu" in g:
+            return int(g["gpu"])
+    return None
+
+
+def parse_smi_metric(obj) -> dict | None:
+    """Shader clock per XCD (MHz, the ``gfx_N`` entries) and socket power (W) of the one GPU in an
+    ``amd-smi metric -c -p`` reply."""
+    gpus = _gpu_entries(obj)
+    if len(gpus) != 1:
+        return None
+    g = gpus[0]
+    clocks = g.get("clock", {})
+    xcd = sorted((k for k in clocks if k.startswith("gfx_") and k[4:].isdigit()), key=lambda k: int(k[4:]))
+    mhz = []
+    for k in xcd:
+        clk = clocks[k].get("clk") if isinstance(clocks[k], dict) else None
+        if isinstance(clk, dict) and isinstance(clk.get("value"), (int, float)):
+            mhz.append(clk["value"])
+    if not mhz:
+        return None
+    res = {"gfx_mhz_per_xcd": mhz, "gfx_mhz_mean": round(sum(mhz) / len(mhz), 1)}
+    top = clocks[xcd[0]].get("max_clk")
+    if isinstance(top, dict) and isinstance(top.get("value"), (int, float)):
+        res["gfx_mhz_max"] = top["value"]
+    power = g.get("power")
+    power = power.get("socket_power") if isinstance(power, dict) else None
+    if isinstance(power, dict) and isinstance(power.get("value"), (int, float)):
+        res["socket_power_w"] = power["value"]
+    return res
+
+
+def clock_sample(step, launch_ms: float, stream, dev, seconds: float = 4.0) -> dict:
+    """The clock under the timed load.  amd-smi reports a clock averaged over a window of about a
+    second, so the same launches run on for ``seconds`` more (outside the timed region; they rewrite
+    the same output) in chunks of about 0.4 s, one chunk always queued ahead, with a reading after
+    each chunk is queued.  Returns the last reading, the mean clock of every reading in order, and
+    the mean launch time over the second half of the chunks (the rate once the clock has settled)."""
+    import torch
+
+    p = torch.cuda.get_device_properties(dev)
+    idx = smi_index(f"{p.pci_domain_id:04x}:{p.pci_bus_id:02x}:{p.pci_device_id:02x}", amd_smi("list"))
+    sel = ["-g", str(idx)] if idx is not None else []
+    per_chunk = max(1, int(400.0 / max(launch_ms, 1e-3)))
+    n_chunks = max(2, int(round(seconds * 1e3 / (per_chunk * launch_ms))))
+
+    spans = []
+
+    def chunk():
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(per_chunk):
+            step()
+        b.record(stream)
+        spans.append((a, b))
+        return b
+
+    pending = [chunk()]
+    series, last, under_load = [], None, False
+    for _ in range(n_chunks - 1):
+        pending.append(chunk())
+        reply = parse_smi_metric(amd_smi("metric", *sel, "-c", "-p"))
+        under_load = not pending[-1].query()
+        if reply is not None:
+            last = reply
+            series.append(reply["gfx_mhz_mean"])
+        pending.pop(0).synchronize()
+    torch.cuda.synchronize()
+    settled = spans[len(spans) // 2:]
+    sustained_ms = sum(a.elapsed_time(b) for a, b in settled) / (per_chunk * len(settled))
+    if last is None:
+        return {"unavailable": "amd-smi gave no clock for this GPU", "sustained_launch_ms": round(sustained_ms, 4)}
+    last["under_load"] = under_load
+    last["gfx_mhz_mean_series"] = series
+    last["launches"] = per_chunk * n_chunks
+    last["sustained_launch_ms"] = round(sustained_ms, 4)
+    static = _gpu_entries(amd_smi("static", *sel, "--asic"))
+    if len(static) == 1 and isinstance(static[0].get("asic"), dict):
+        last["market_name"] = static[0]["asic"].get("market_name")
+    # the dense bf16 peak at the clock the XCDs ran at
+    last["mfma_peak_at_clock_tflops"] = round(p.multi_processor_count * last["gfx_mhz_mean"] * 1e6 * 4096 / 1e12, 1)
+    return last
+
+
+def run_env(dev) -> dict:
+    """Versions and build flags the figures were taken with."""
+    import torch
+
+    from bf16_forward_attention_amd import build
+
+    p = torch.cuda.get_device_properties(dev)
+    try:
+        with open("/opt/rocm/.info/version") as f:
+            rocm = f.read().strip()
+    except OSError:
+        rocm = None
+    return {"rocm": rocm, "torch": torch.__version__, "hip": torch.version.hip, "device": p.name,
+            "arch": p.gcnArchName, "cus": p.multi_processor_count,
+            "hipcc_flags": " ".join(build.HIPCC_FLAGS)}
 
 
 def parse():
@@ -276,6 +403,9 @@ def main():
         log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
         del src, dst
 
+    clock = clock_sample(step, float(per.mean()), stream, dev)
+    clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
+    log(f"[bench] clock {clock}")
     out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -295,6 +425,8 @@ def main():
                                + (" + attn_merge_kernel" if ws_bytes else ""),
                      "launch_ms_mean": round(float(per.mean()), 4),
                      "launch_ms_median": round(float(np.median(per)), 4)},
+        "clock": clock,
+        "env": run_env(dev),
     }
     if not args.no_cpu_baseline:
         from tests.gate import gate
@@ -371,6 +503,9 @@ def main_varlen(args):
     achieved = flops / (per.mean() * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, per-launch mean {per.mean():.3f} median {np.median(per):.3f} ms "
         f"-> {value:.1f} TFLOP/s")
+    clock = clock_sample(step, float(per.mean()), stream, dev)
+    clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
+    log(f"[bench] clock {clock}")
     out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     result = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -388,6 +523,8 @@ def main_varlen(args):
                      "kernel": f"attn_fwd_kernel<{mode.upper()}, varlen{', causal' if wl.mask != 'none' else ''}>",
                      "launch_ms_mean": round(float(per.mean()), 4),
                      "launch_ms_median": round(float(np.median(per)), 4)},
+        "clock": clock,
+        "env": run_env(dev),
     }
     if not args.no_cpu_baseline:
         import oracle

@@ -73,3 +73,44 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, "bench.py", "--gpus", "2"], cwd=ROOT, capture_output=True, text=True,
                        timeout=120)
     assert r.returncode == 2 and "one GPU" in (r.stdout + r.stderr)
+
+
+def _smi_reply(mhz, power=None, wrap=True):
+    clock = {f"gfx_{i}": {"clk": {"value": c, "unit": "MHz"}, "min_clk": {"value": 500, "unit": "MHz"},
+                          "max_clk": {"value": 2400, "unit": "MHz"}} for i, c in enumerate(mhz)}
+    clock["mem_0"] = {"clk": {"value": 2000, "unit": "MHz"}}
+    g = {"gpu": 0, "clock": clock}
+    if power is not None:
+        g["power"] = {"socket_power": {"value": power, "unit": "W"}, "gfx_voltage": "N/A"}
+    return {"gpu_data": [g]} if wrap else [g]
+
+
+def test_smi_metric_parsing():
+    mhz = [1815, 1720, 1795, 1718, 1804, 1713, 1769, 1688, 1700, 1701, 1702]
+    res = bench.parse_smi_metric(_smi_reply(mhz, power=1380))
+    # XCDs in index order (gfx_10 after gfx_9), memory clock left out
+    assert res["gfx_mhz_per_xcd"] == mhz
+    assert res["gfx_mhz_mean"] == round(sum(mhz) / len(mhz), 1)
+    assert res["gfx_mhz_max"] == 2400 and res["socket_power_w"] == 1380
+    assert "socket_power_w" not in bench.parse_smi_metric(_smi_reply([100, 200], wrap=False))
+    # no reply, no GPU, two GPUs (ambiguous), a clock field that is not a number
+    assert bench.parse_smi_metric(None) is None
+    assert bench.parse_smi_metric({"gpu_data": []}) is None
+    two = _smi_reply([1700])
+    two["gpu_data"].append(dict(two["gpu_data"][0], gpu=1))
+    assert bench.parse_smi_metric(two) is None
+    assert bench.parse_smi_metric(_smi_reply(["N/A"])) is None
+
+
+def test_smi_index_by_pci_address():
+    listing = [{"gpu": 0, "bdf": "0000:05:00.0"}, {"gpu": 1, "bdf": "0000:75:00.0"}]
+    assert bench.smi_index("0000:75:00", listing) == 1
+    assert bench.smi_index("0000:05:00", {"gpu_data": listing}) == 0
+    assert bench.smi_index("0000:99:00", listing) is None
+    assert bench.smi_index("0000:05:00", None) is None
+
+
+def test_amd_smi_missing_tool(monkeypatch):
+    monkeypatch.setattr(bench.shutil, "which", lambda name: None)
+    monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: (_ for _ in ()).throw(OSError("no such file")))
+    assert bench.amd_smi("list") is None
