@@ -23,7 +23,7 @@ BSHD, RTNE.  Prints one JSON line:
   env        ROCm and torch versions, the device, the hipcc flags of the build
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-       [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S]
+       [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S] [--no-split] [--no-clock]
 """
 from __future__ import annotations
 
@@ -180,6 +180,9 @@ def parse():
     p.add_argument("--mode", default=None, help="rounding mode (default: the workload's first)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-split", action="store_true", help="always run single-pass (no key-range split)")
+    p.add_argument("--no-clock", action="store_true",
+                   help="leave out the clock sample (its ~4 s of extra launches and the amd-smi queries), e.g. "
+                        "under a profiler")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for the sample")
     p.add_argument("--parity-rows", type=int, default=256)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -403,8 +406,11 @@ def main():
         log(f"[bench] calibration copy of {args.calibrate_copy_mib} MiB done")
         del src, dst
 
-    clock = clock_sample(step, float(per.mean()), stream, dev)
-    clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
+    if args.no_clock:
+        clock = {"skipped": "--no-clock"}
+    else:
+        clock = clock_sample(step, float(per.mean()), stream, dev)
+        clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
     log(f"[bench] clock {clock}")
     out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     result = {
@@ -503,8 +509,11 @@ def main_varlen(args):
     achieved = flops / (per.mean() * 1e-3) / 1e12
     log(f"[bench] {ms_per_step:.3f} ms/step, per-launch mean {per.mean():.3f} median {np.median(per):.3f} ms "
         f"-> {value:.1f} TFLOP/s")
-    clock = clock_sample(step, float(per.mean()), stream, dev)
-    clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
+    if args.no_clock:
+        clock = {"skipped": "--no-clock"}
+    else:
+        clock = clock_sample(step, float(per.mean()), stream, dev)
+        clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
     log(f"[bench] clock {clock}")
     out_bits = o.view(torch.int16).cpu().numpy().view(np.uint16)
     result = {
