@@ -54,7 +54,7 @@ def amd_smi(*args):
     """One ``amd-smi ... --json`` query, parsed; None where the tool is missing or fails."""
     exe = shutil.which("amd-smi") or "/opt/rocm/bin/amd-smi"
     try:
-        out = subprocess.run([exe, *args, "--json"], capture_output=True, text=True, timeout=20).stdout
+        out = subprocess.run([exe, *args, "--json"], capture_output=True, text=True, timeout=10).stdout
         starts = [i for i in (out.find("{"), out.find("[")) if i >= 0]
         return json.JSONDecoder().raw_decode(out[min(starts):])[0] if starts else None
     except (OSError, subprocess.SubprocessError, ValueError):
@@ -128,14 +128,17 @@ def clock_sample(step, launch_ms: float, stream, dev, seconds: float = 4.0) -> d
         return b
 
     pending = [chunk()]
-    series, last, under_load = [], None, False
+    series, last, under_load, asking = [], None, False, True
     for _ in range(n_chunks - 1):
         pending.append(chunk())
-        reply = parse_smi_metric(amd_smi("metric", *sel, "-c", "-p"))
-        under_load = not pending[-1].query()
-        if reply is not None:
-            last = reply
-            series.append(reply["gfx_mhz_mean"])
+        if asking:
+            reply = parse_smi_metric(amd_smi("metric", *sel, "-c", "-p"))
+            under_load = not pending[-1].query()
+            if reply is None:
+                asking = False  # no tool, no clock in its reply, or a time-out: ask no more
+            else:
+                last = reply
+                series.append(reply["gfx_mhz_mean"])
         pending.pop(0).synchronize()
     torch.cuda.synchronize()
     settled = spans[len(spans) // 2:]
