@@ -219,8 +219,8 @@ def attn_rows_varlen(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, ro
 
     ``q`` is [total_q, H, 128] and ``k``/``v`` [total_k, H_kv, 128] bf16 bits:
     sequence b holds query rows cu_q[b] .. cu_q[b+1]-1 and key rows
-    cu_k[b] .. cu_k[b+1]-1, and attends only within itself (the survey's
-    variable-length batching: FlashAttention's packed "cu_seqlens" layout).
+    cu_k[b] .. cu_k[b+1]-1, and attends only within itself (variable-length
+    batching in FlashAttention's packed "cu_seqlens" layout).
     Each sequence is the fixed-length problem B=1, Sq = its query rows, Sk = its
     key rows in BSHD, handed to ``attn_rows`` as such; a sequence with no key
     gives NaN rows (the 0/0 of an empty softmax).  ``rows`` are (t, h) pairs

@@ -51,8 +51,8 @@
  * Log-sum-exp.  Per query row, lse = log(sum_j exp(s_j)) over the keys the
  * row sees (natural log, the logits of step 2), the per-row statistic the
  * FlashAttention family keeps for a backward pass or for merging key ranges;
- * the pages do not discuss it (an extension the survey lists after GQA and
- * varlen).  Evaluated as m + log(l) from steps 3-4 when m is finite; -Inf
+ * the pages do not discuss it (an extension beside grouped heads and packed
+ * batches).  Evaluated as m + log(l) from steps 3-4 when m is finite; -Inf
  * when the row sees no key or only -Inf logits (the log of an empty or zero
  * sum); NaN when m is NaN or +Inf (the rows whose output is NaN as well).
  *

@@ -2,7 +2,7 @@
 the keys a row sees, with -Inf for a row that sees none (or only -Inf
 logits) and NaN where the row's output is NaN.  The pages do not discuss it:
 it is the per-row statistic the FlashAttention family keeps for a backward
-pass or for merging key ranges, which the survey lists after GQA and varlen.
+pass or for merging key ranges (an extension beside grouped heads and packed batches).
 Checked against exact logarithms of counts, numpy's logaddexp, scipy's and
 torch's logsumexp on the same float64 logits, a dominant key, and the
 special values.
