@@ -114,3 +114,12 @@ def test_amd_smi_missing_tool(monkeypatch):
     monkeypatch.setattr(bench.shutil, "which", lambda name: None)
     monkeypatch.setattr(bench.subprocess, "run", lambda *a, **k: (_ for _ in ()).throw(OSError("no such file")))
     assert bench.amd_smi("list") is None
+
+
+def test_profiler_detection(monkeypatch):
+    monkeypatch.setenv("LD_PRELOAD", "/opt/rocm/lib/rocprofiler-sdk/librocprofiler-sdk-tool.so:/x/lib.so")
+    assert bench.under_profiler()
+    monkeypatch.setenv("LD_PRELOAD", "/usr/lib/libother.so")
+    assert not bench.under_profiler()
+    monkeypatch.delenv("LD_PRELOAD")
+    assert not bench.under_profiler()
