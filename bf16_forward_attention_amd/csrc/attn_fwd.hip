@@ -225,16 +225,17 @@ __device__ __forceinline__ i32x4 make_rsrc(const void* base, uint32_t num_record
 
 // One direct-to-LDS load: 16 bytes per lane from rsrc + voffset land at
 // lds_base + 16 * lane.  Written as a single-instruction asm wrapper (plus
-// the M0 set-up and the one-cycle M0 hazard wait) so the compiler does not
+// the one-cycle M0 hazard wait) so the compiler does not
 // track it as an LDS write: it would otherwise wait for every such load in
 // flight before each later LDS read, since it cannot tell which stage a load
 // fills.  The kernel orders these loads itself with s_waitcnt vmcnt and the
-// workgroup barrier (loads complete in order).  M0 is a reserved register
-// that the compiler itself sets right before each of its own uses.
+// workgroup barrier (loads complete in order).  The LDS address goes in
+// through an M0 operand, so the compiler writes M0 itself and knows it is
+// taken; the s_nop covers the one wait state between that write and the load.
 __device__ __forceinline__ void lds_dma_b128(i32x4 rsrc, uint32_t lds_base, uint32_t voffset) {
-  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+  asm volatile("s_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :
-               : "s"(lds_base), "v"(voffset), "s"(rsrc)
+               : "{m0}"(lds_base), "v"(voffset), "s"(rsrc)
                : "memory");
 }
 
