@@ -1,4 +1,5 @@
-"""Fused non-causal bf16 forward attention (head_dim 128) for MI355X.
+"""Fused bf16 forward attention (head_dim 128) for MI355X: without a mask or with a
+causal one, grouped K/V heads, packed variable-length batches, per-row log-sum-exp.
 
 Thin binding over the C ABI in ``include/attn_fwd.h``: argument marshalling
 only, every step of the computation runs in the HIP library

@@ -108,3 +108,25 @@ def diagonal_dominant(B, H, Sq, Sk, off, seed=0):
             q[:, :, i, 1 + i] = bf(128.0)
             k[:, :, j, 1 + i] = bf(128.0)
     return q, k, v
+
+
+def subnormal_bits(shape, seed: int, tensor_id: int = 9) -> np.ndarray:
+    """bf16 subnormals: random sign, significand 1..127 (values k * 2^-133),
+    from the seeded counter-based stream."""
+    n = int(np.prod(shape))
+    u = synth.u64_at(synth.stream_key(seed, tensor_id), np.arange(n, dtype=np.uint64))
+    mag = (u % np.uint64(127)).astype(np.uint16) + np.uint16(1)
+    sign = ((u >> np.uint64(32)) & np.uint64(1)).astype(np.uint16) << np.uint16(15)
+    return (mag | sign).reshape(shape)
+
+
+def scaled_bits(shape, seed: int, exp_shift: int, tensor_id: int = 10) -> np.ndarray:
+    """bf16 values u * 2^exp_shift with u ~ U(-1.9, 1.9) (normal bf16 values of
+    that range, zero kept), by adding ``exp_shift`` to the exponent field."""
+    n = int(np.prod(shape))
+    b = synth.uniform_bf16(seed, tensor_id, n, -1.9, 1.9).astype(np.int32)
+    e = (b >> 7) & 0xFF
+    if np.any((e != 0) & ((e + exp_shift < 1) | (e + exp_shift > 254))):
+        raise ValueError("shift leaves the normal bf16 range")
+    out = np.where(e != 0, b + (exp_shift << 7), b)
+    return out.astype(np.uint16).reshape(shape)

@@ -7,6 +7,12 @@ head, plus the rows that sit on tile boundaries and at the ragged end of the
 query range.  Properties that hold at any size are checked on every row:
 repeated launches give identical bits, and in the stressed workload the NaN
 rows are exactly the ones the injected K specials must poison.
+
+Then every row of the self-attention (B=4 H=16 8192x8192), cross-attention
+(B=2 H=24 4097x32771) and stressed (B=1 H=40 32760x32760) workloads is
+compared with the oracle, in chunks of heads (each chunk a test of its own, so
+progress shows), every launch configuration the sampled test ran.  On the
+inputs drawn N(0,1) the RMS guard of tests/gate.py holds as well.
 """
 import time
 
@@ -17,7 +23,7 @@ import torch
 import bf16_forward_attention_amd as attn
 import oracle
 from bf16_forward_attention_amd import synth
-from tests.gate import gate
+from tests.gate import gate, merge
 from tests.gpu_util import MODES, Dev, say
 
 pytestmark = pytest.mark.gpu
@@ -54,6 +60,15 @@ def _gather(out_stored, layout, rows):
     return np.stack([logical[b, h, i] for b, h, i in rows])
 
 
+# outputs of the full-size launches, kept for the every-row tests of the same workload:
+# name -> (wl, inputs, {(entry, mode): stored output bits})
+_OUTPUTS = {}
+
+
+def _standard_normal(wl) -> bool:
+    return wl.qk_sigma == 1.0 and wl.v_dist == "normal" and not wl.scaled_row_fraction and not wl.inject_k_specials
+
+
 def _run_config(name):
     wl = synth.WORKLOADS[name]
     t0 = time.perf_counter()
@@ -76,10 +91,12 @@ def _run_config(name):
         res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
         say(f"  {name} {mode}: {res.summary()}")
         assert res.ok, f"{name} {mode}: {res.summary()}"
-        outs[mode] = out
+        if _standard_normal(wl):
+            assert res.rms_guard_ok, f"{name} {mode}: RMS guard: {res.summary()}"
+        outs[("single", mode)] = out
     # determinism over the whole tensor
     again = dev.run(wl.modes[0])
-    assert np.array_equal(again, outs[wl.modes[0]]), "repeated launch changed the output"
+    assert np.array_equal(again, outs[("single", wl.modes[0])]), "repeated launch changed the output"
     # the key-range-splitting entry point, where this shape splits (the call the benchmark times then)
     if wl.mask == "none" and wl.kv_heads == wl.H:
         split_bytes = attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
@@ -91,8 +108,43 @@ def _run_config(name):
             res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
             say(f"  {name} {mode} split: {res.summary()}")
             assert res.ok, f"{name} {mode} split: {res.summary()}"
+            if _standard_normal(wl):
+                assert res.rms_guard_ok, f"{name} {mode} split: RMS guard: {res.summary()}"
+            outs[("split", mode)] = out
         assert np.array_equal(out, dev.run(wl.modes[-1], split=True)), "split launch not deterministic"
-    return wl, inp, outs
+    _OUTPUTS[name] = (wl, inp, outs)
+    return wl, inp, {mode: outs[("single", mode)] for mode in wl.modes}
+
+
+N_CHUNKS = {"self8k": 4, "cross_odd": 4, "dit_stress": 8}
+
+
+def _every_row_chunk(name, chunk):
+    """Compare every row of a chunk of heads with the oracle, for every stored launch."""
+    if name not in _OUTPUTS:
+        _run_config(name)
+    wl, inp, outs = _OUTPUTS[name]
+    n_heads = wl.B * wl.H
+    heads = range(chunk * n_heads // N_CHUNKS[name], (chunk + 1) * n_heads // N_CHUNKS[name])
+    results = {key: [] for key in outs}
+    t0 = time.perf_counter()
+    logical = {key: synth.to_logical(out, wl.layout) for key, out in outs.items()}
+    for bh in heads:
+        b, h = divmod(bh, wl.H)
+        rows = [(b, h, i) for i in range(wl.Sq)]
+        ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask=wl.mask)
+        for (entry, mode), lg in logical.items():
+            results[(entry, mode)].append(gate(lg[b, h], rd[:, MODES.index(mode)], ex))
+    say(f"  {name} heads {heads.start}..{heads.stop - 1}: oracle and gate in {time.perf_counter() - t0:.1f} s")
+    for key, parts in results.items():
+        res = merge(parts)
+        say(f"  {name} {key[0]} {key[1]} every row of heads {heads.start}..{heads.stop - 1}: {res.summary()}")
+        assert res.n > 0
+        assert res.ok, f"{name} {key}: {res.summary()}"
+        if _standard_normal(wl):
+            assert res.rms_guard_ok, f"{name} {key}: RMS guard: {res.summary()}"
+    if chunk == N_CHUNKS[name] - 1:
+        del _OUTPUTS[name]
 
 
 @pytest.mark.timeout(600)
@@ -102,9 +154,23 @@ def test_self_attention_8k():
 
 
 @pytest.mark.timeout(600)
+@pytest.mark.parametrize("chunk", range(N_CHUNKS["self8k"]))
+def test_self_attention_8k_every_row(chunk):
+    # all 524,288 rows, 16 heads per chunk
+    _every_row_chunk("self8k", chunk)
+
+
+@pytest.mark.timeout(600)
 def test_cross_attention_odd_lengths():
     # B=2 H=24 Sq=4097 Sk=32771 BSHD RTZ: ragged q-tile and ragged last key tile
     _run_config("cross_odd")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("chunk", range(N_CHUNKS["cross_odd"]))
+def test_cross_attention_odd_lengths_every_row(chunk):
+    # all 196,656 rows of the single pass and of the key-range split (the launch the benchmark times)
+    _every_row_chunk("cross_odd", chunk)
 
 
 @pytest.mark.timeout(900)
@@ -137,6 +203,14 @@ def test_stressed_logits_with_k_specials():
     assert not np.any(((out & 0x7FFF) == 0x7F80)), "an output element is infinite"
     # the x64-scaled rows were sampled too: make sure some were checked
     say(f"  NaN rows: {int(nan_rows.sum())} of {nan_rows.size}")
+
+
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("chunk", range(N_CHUNKS["dit_stress"]))
+def test_stressed_logits_every_row(chunk):
+    # all 1,310,400 rows (5 heads per chunk): every x64-scaled row, every row of the three heads with
+    # a K special, and the rest
+    _every_row_chunk("dit_stress", chunk)
 
 
 @pytest.mark.timeout(600)
