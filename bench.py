@@ -21,9 +21,15 @@ BSHD, RTNE.  Prints one JSON line:
              about 4 s more of the same launches right after the timed region, and
              the rate over the last 2 s of them (sustained_tflops)
   env        ROCm and torch versions, the device, the hipcc flags of the build
+  sweep      (with the default workload, or --sweep) the other configurations of 8K and
+             longer, each timed alone the same way after the headline: the 128K
+             long-context workload in all three rounding modes, the 4097 x 32771
+             cross-attention and the stressed 32760 x 32760 workload, each with its
+             rate, share of the peak, clock and a parity sample against the oracle
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S] [--no-split] [--no-clock]
+       [--sweep | --no-sweep] [--sweep-seconds S]
 """
 from __future__ import annotations
 
@@ -195,6 +201,12 @@ def parse():
                         "it is left out by itself under rocprofv3")
     p.add_argument("--cpu-seconds", type=float, default=15.0, help="target oracle wall time for the sample")
     p.add_argument("--parity-rows", type=int, default=256)
+    p.add_argument("--sweep", dest="sweep", action="store_true", default=None,
+                   help="also time the other configurations of 8K and longer (default: with the default workload)")
+    p.add_argument("--no-sweep", dest="sweep", action="store_false")
+    p.add_argument("--sweep-seconds", type=float, default=1.5, help="timed launches per sweep configuration")
+    p.add_argument("--sweep-warmup", type=int, default=3)
+    p.add_argument("--sweep-clock-seconds", type=float, default=3.0)
     p.add_argument("--calibrate-copy-mib", type=int, default=0,
                    help="also run one device-to-device copy of this many MiB (a reference kernel of known "
                         "traffic for the FETCH_SIZE/WRITE_SIZE counters)")
@@ -309,6 +321,184 @@ def measured_traffic(workload: str):
     return int(round((fetch + write) * 1024))
 
 
+def make_step(attn, wl, mode, q, k, v, o, stream, dev, no_split):
+    """The call one step makes for workload ``wl`` in ``mode`` on resident tensors:
+    attn_fwd_bf16_ws / attn_fwd_bf16_gqa_ws with a preallocated workspace where the shape
+    splits its key ranges, attn_fwd_bf16_gqa (grouped), attn_fwd_bf16_masked (causal) or
+    attn_fwd_bf16 otherwise.  Returns (step, description, workspace bytes, workspace)."""
+    import torch
+
+    masked = wl.mask != "none"
+    grouped = wl.kv_heads != wl.H
+    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
+    if no_split:
+        ws_bytes = 0
+    elif masked or grouped:
+        ws_bytes = attn.attn_fwd_bf16_gqa_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk, attn.MASKS[wl.mask])
+    else:
+        ws_bytes = attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
+              attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
+    if ws_bytes > 0 and (masked or grouped):
+        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan_masked(wl.B * wl.H, wl.Sq, wl.Sk,
+                                                                         attn.MASKS[wl.mask], n_cu)
+        entry = (f"attn_fwd_bf16_gqa_ws(H_kv={wl.kv_heads}, {wl.mask}): {whole} work items whole, {items} split "
+                 f"into {splits} key ranges (of up to {tps} tiles), {ws_bytes} B workspace")
+    elif ws_bytes > 0:
+        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan(wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64),
+                                                                  n_cu)
+        entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
+                 f"{tps} tiles, {ws_bytes} B workspace")
+    elif grouped:
+        entry = f"attn_fwd_bf16_gqa(H_kv={wl.kv_heads}, {wl.mask})"
+    elif masked:
+        entry = f"attn_fwd_bf16_masked({wl.mask})"
+    else:
+        entry = "attn_fwd_bf16"
+
+    def step():
+        if ws_bytes > 0 and (masked or grouped):
+            st = attn.attn_fwd_bf16_gqa_ws(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads,
+                                           wl.Sq, wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], ws.data_ptr(),
+                                           ws_bytes, stream.cuda_stream)
+        elif ws_bytes > 0:
+            st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
+        elif grouped:
+            st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads, wl.Sq,
+                                        wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], stream.cuda_stream)
+        elif masked:
+            st = attn.attn_fwd_bf16_masked(*args_c, attn.MASKS[wl.mask], stream.cuda_stream)
+        else:
+            st = attn.attn_fwd_bf16(*args_c, stream.cuda_stream)
+        if st != 0:
+            raise attn.AttnError(st)
+
+    return step, entry, ws_bytes, ws
+
+
+def time_launches(step, stream, steps):
+    """``steps`` launches, each bracketed by HIP events on the launch stream: (ms per step over
+    the whole region, per-launch times in ms)."""
+    import torch
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
+    torch.cuda.synchronize()
+    for i in range(steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    per = np.array([a.elapsed_time(b) for a, b in zip(starts, ends)])
+    return starts[0].elapsed_time(ends[-1]) / steps, per
+
+
+# The configurations of sequence length 8K and longer besides the headline one, timed after it
+# in the same run: the long-context workload in every rounding mode, the cross-attention with odd
+# lengths and the stressed diffusion-transformer-like workload.
+SWEEP = (("long128k", "rtne"), ("long128k", "rtna"), ("long128k", "rtz"), ("cross_odd", "rtz"),
+         ("dit_stress", "rtna"))
+
+
+def sweep_parity_rows(inp, n=128):
+    """Rows the sweep's parity sample checks: the workload's own checked subset where it has one,
+    else seeded rows of every head plus each head's last row; the stressed workload adds some of
+    its x64-scaled rows and rows of the heads with K specials."""
+    from bf16_forward_attention_amd import synth
+
+    wl = inp.wl
+    n_heads = wl.B * wl.H
+    per = max(1, n // n_heads)
+    rows = set()
+    for bh in range(n_heads):
+        b, h = divmod(bh, wl.H)
+        if wl.checked_rows_per_head:
+            subset = synth.floyd_sample(wl.seed, synth.TID_SUBSET, wl.Sq, wl.checked_rows_per_head, stream=bh)
+            rows.update((b, h, i) for i in subset[:per])
+        else:
+            rows.update(head_rows(wl, per, b, h, stream=(1 << 22) + bh))
+            rows.add((b, h, wl.Sq - 1))
+    for f in inp.scaled_rows[:16]:
+        rows.add((f // (wl.H * wl.Sq), (f // wl.Sq) % wl.H, f % wl.Sq))
+    for _, b, h, _, _ in inp.specials:
+        rows.update(head_rows(wl, 8, b, h, stream=(1 << 23) + b * wl.H + h))
+    return sorted(rows)
+
+
+def run_sweep(args, dev):
+    """Time each SWEEP configuration on its own (inputs resident, the same launch protocol as the
+    headline), with the clock under it and a parity sample of its output against the oracle."""
+    import torch
+
+    import bf16_forward_attention_amd as attn
+    import oracle
+    from bf16_forward_attention_amd import synth
+    from tests.gate import gate
+
+    stream = torch.cuda.current_stream(dev)
+    out = []
+    loaded = None
+    for name, mode in SWEEP:
+        wl = synth.WORKLOADS[name]
+        if loaded is None or loaded[0].wl.name != name:
+            loaded = None
+            torch.cuda.empty_cache()
+            t0 = time.perf_counter()
+            inp = synth.generate(wl)
+            t = lambda a: torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+            loaded = (inp, t(inp.q), t(inp.k), t(inp.v))
+            log(f"[bench] sweep: generated {name} in {time.perf_counter() - t0:.1f} s")
+            rows = sweep_parity_rows(inp)
+            t0 = time.perf_counter()
+            ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask=wl.mask)
+            log(f"[bench] sweep: oracle on {len(rows)} rows of {name} in {time.perf_counter() - t0:.1f} s")
+        inp, q, k, v = loaded
+        o = torch.empty_like(q)
+        step, entry, ws_bytes, _ws = make_step(attn, wl, mode, q, k, v, o, stream, dev, args.no_split)
+        flops = workload_flops(wl)
+        for _ in range(args.sweep_warmup):
+            step()
+        torch.cuda.synchronize()
+        # about args.sweep_seconds of timed launches, at least 10
+        probe_ms, _ = time_launches(step, stream, 2)
+        steps = int(min(args.steps, max(10, round(args.sweep_seconds * 1e3 / max(probe_ms, 1e-3)))))
+        ms_per_step, per = time_launches(step, stream, steps)
+        achieved = flops / (per.mean() * 1e-3) / 1e12
+        value = flops / (ms_per_step * 1e-3) / 1e12
+        log(f"[bench] sweep {name} {mode}: {ms_per_step:.3f} ms/step over {steps} steps -> {value:.1f} TFLOP/s "
+            f"({achieved / PEAK_BF16_TFLOPS:.4f} of peak)")
+        if args.no_clock or under_profiler():
+            clock = {"skipped": "--no-clock" if args.no_clock else "under rocprofv3"}
+        else:
+            clock = clock_sample(step, float(per.mean()), stream, dev, seconds=args.sweep_clock_seconds)
+            clock["sustained_tflops"] = round(flops / (clock["sustained_launch_ms"] * 1e-3) / 1e12, 1)
+            clock = {key: clock[key] for key in ("gfx_mhz_mean", "socket_power_w", "mfma_peak_at_clock_tflops",
+                                                 "sustained_tflops", "sustained_launch_ms", "under_load",
+                                                 "unavailable") if key in clock}
+        logical = synth.to_logical(o.view(torch.int16).cpu().numpy().view(np.uint16), wl.layout)
+        got = np.stack([logical[b, h, i] for b, h, i in rows])
+        res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)
+        log(f"[bench] sweep parity {name} {mode}: {res.summary()}")
+        out.append({
+            "workload": f"{wl.name}: B={wl.B} H={wl.H} Sq={wl.Sq} Sk={wl.Sk} d=128 {wl.layout.upper()} {mode.upper()}",
+            "round_mode": mode, "entry_point": entry, "steps": steps, "warmup": args.sweep_warmup,
+            "ms_per_step": round(ms_per_step, 4), "tflops": round(value, 2),
+            "roofline": {"bound": "mfma", "achieved": round(achieved, 2), "peak": round(PEAK_BF16_TFLOPS, 1),
+                         "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                         "traffic": measured_traffic(wl.name),
+                         "launch_ms_mean": round(float(per.mean()), 4),
+                         "launch_ms_median": round(float(np.median(per)), 4)},
+            "clock": clock,
+            "parity": {"rows": len(rows), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
+                       "strict_ulp_hist": res.strict_hist, "rms_excess": round(res.rms_excess, 6)},
+        })
+        del o, step, _ws
+    loaded = None
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -337,69 +527,17 @@ def main():
     stream = torch.cuda.current_stream(dev)
     masked = wl.mask != "none"
     grouped = wl.kv_heads != wl.H
-    n_cu = torch.cuda.get_device_properties(dev).multi_processor_count
-    if args.no_split:
-        ws_bytes = 0
-    elif masked or grouped:
-        ws_bytes = attn.attn_fwd_bf16_gqa_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk, attn.MASKS[wl.mask])
-    else:
-        ws_bytes = attn.attn_fwd_bf16_workspace_size(wl.B, wl.H, wl.Sq, wl.Sk)
-    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-    args_c = (q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), wl.B, wl.H, wl.Sq, wl.Sk,
-              attn.LAYOUTS[wl.layout], attn.ROUND_MODES[mode])
-    if ws_bytes > 0 and (masked or grouped):
-        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan_masked(wl.B * wl.H, wl.Sq, wl.Sk,
-                                                                         attn.MASKS[wl.mask], n_cu)
-        entry = (f"attn_fwd_bf16_gqa_ws(H_kv={wl.kv_heads}, {wl.mask}): {whole} work items whole, {items} split "
-                 f"into {splits} key ranges (of up to {tps} tiles), {ws_bytes} B workspace")
-    elif ws_bytes > 0:
-        whole, items, splits, tps = attn.attn_fwd_bf16_split_plan(wl.B * wl.H * -(-wl.Sq // 256), -(-wl.Sk // 64),
-                                                                  n_cu)
-        entry = (f"attn_fwd_bf16_ws: {whole} work items whole, {items} split into {splits} key ranges of "
-                 f"{tps} tiles, {ws_bytes} B workspace")
-    elif grouped:
-        entry = f"attn_fwd_bf16_gqa(H_kv={wl.kv_heads}, {wl.mask})"
-    elif masked:
-        entry = f"attn_fwd_bf16_masked({wl.mask})"
-    else:
-        entry = "attn_fwd_bf16"
+    step, entry, ws_bytes, ws = make_step(attn, wl, mode, q, k, v, o, stream, dev, args.no_split)
     log(f"[bench] entry point: {entry}")
-
-    def step():
-        if ws_bytes > 0 and (masked or grouped):
-            st = attn.attn_fwd_bf16_gqa_ws(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads,
-                                           wl.Sq, wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], ws.data_ptr(),
-                                           ws_bytes, stream.cuda_stream)
-        elif ws_bytes > 0:
-            st = attn.attn_fwd_bf16_ws(*args_c, ws.data_ptr(), ws_bytes, stream.cuda_stream)
-        elif grouped:
-            st = attn.attn_fwd_bf16_gqa(args_c[0], args_c[1], args_c[2], args_c[3], 0, wl.B, wl.H, wl.kv_heads, wl.Sq,
-                                        wl.Sk, args_c[8], args_c[9], attn.MASKS[wl.mask], stream.cuda_stream)
-        elif masked:
-            st = attn.attn_fwd_bf16_masked(*args_c, attn.MASKS[wl.mask], stream.cuda_stream)
-        else:
-            st = attn.attn_fwd_bf16(*args_c, stream.cuda_stream)
-        if st != 0:
-            raise attn.AttnError(st)
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
     log(f"[bench] timing {args.steps} steps")
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
     t_wall = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
+    ms_per_step, per = time_launches(step, stream, args.steps)
     wall_ms = (time.perf_counter() - t_wall) * 1e3
-    per = np.array([s.elapsed_time(e) for s, e in zip(starts, ends)])
-    total_ms = starts[0].elapsed_time(ends[-1])
-    ms_per_step = total_ms / args.steps
     flops = workload_flops(wl)
     value = flops / (ms_per_step * 1e-3) / 1e12
     achieved = flops / (per.mean() * 1e-3) / 1e12
@@ -454,8 +592,12 @@ def main():
         got = np.stack([logical[b, h, i] for b, h, i in rows])
         res = gate(got, rd[:, ("rtne", "rtna", "rtz").index(mode)], ex)
         result["parity"] = {"rows": len(rows), "ok": res.ok, "max_row_ulps": round(res.max_row_ulps, 3),
-                            "strict_ulp_hist": res.strict_hist}
+                            "strict_ulp_hist": res.strict_hist, "rms_excess": round(res.rms_excess, 6),
+                            "rms_floor_violations": res.rms_floor_violations}
         log(f"[bench] parity {res.summary()}")
+    if args.sweep or (args.sweep is None and args.workload == "self8k"):
+        del q, k, v, o, ws, step
+        result["sweep"] = run_sweep(args, dev)
     print(json.dumps(result), flush=True)
 
 

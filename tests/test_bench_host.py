@@ -123,3 +123,30 @@ def test_profiler_detection(monkeypatch):
     assert not bench.under_profiler()
     monkeypatch.delenv("LD_PRELOAD")
     assert not bench.under_profiler()
+
+
+def test_sweep_covers_the_long_configurations_and_their_modes():
+    names = {(n, m) for n, m in bench.SWEEP}
+    assert {("long128k", m) for m in ("rtne", "rtna", "rtz")} <= names
+    assert ("cross_odd", "rtz") in names and ("dit_stress", "rtna") in names
+    for n, m in bench.SWEEP:
+        wl = synth.WORKLOADS[n]
+        assert m in wl.modes and max(wl.Sq, wl.Sk) >= 8192
+
+
+def test_sweep_parity_rows():
+    # the long-context rows come from its own checked subset; the stressed workload's sample holds
+    # x64-scaled rows and rows of every head with a K special
+    wl = synth.WORKLOADS["long128k"]
+    inp = synth.Inputs(wl, None, None, None)
+    rows = bench.sweep_parity_rows(inp)
+    checked = set(synth.checked_rows(wl))
+    assert len(rows) >= 128 and set(rows) <= checked
+    wl = synth.WORKLOADS["dit_stress"]
+    inp = synth.Inputs(wl, None, None, None, synth.scaled_row_list(wl), synth.special_list(wl))
+    rows = set(bench.sweep_parity_rows(inp))
+    scaled = {(f // (wl.H * wl.Sq), (f // wl.Sq) % wl.H, f % wl.Sq) for f in inp.scaled_rows[:16]}
+    assert scaled <= rows
+    for _, b, h, _, _ in inp.specials:
+        assert sum(1 for r in rows if r[:2] == (b, h)) >= 8
+    assert all(0 <= i < wl.Sq for _, _, i in rows)
