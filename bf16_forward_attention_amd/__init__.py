@@ -90,6 +90,9 @@ def load_library():
         lib.attn_fwd_bf16_gqa_ws.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_int, vp, i64, vp]
         lib.attn_fwd_bf16_gqa_ws.restype = ctypes.c_int
+        lib.attn_fwd_bf16_gqa_noalloc.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, ctypes.c_int,
+                                                  ctypes.c_int, ctypes.c_int, vp]
+        lib.attn_fwd_bf16_gqa_noalloc.restype = ctypes.c_int
         lib.attn_fwd_bf16_gqa_workspace_size.argtypes = [i64, i64, i64, i64, ctypes.c_int, ctypes.POINTER(i64)]
         lib.attn_fwd_bf16_gqa_workspace_size.restype = ctypes.c_int
         lib.attn_fwd_bf16_split_plan_masked.argtypes = [i64, i64, i64, ctypes.c_int, i64, ctypes.POINTER(i64)]
@@ -159,6 +162,14 @@ def attn_fwd_bf16_gqa_ws(q: int, k: int, v: int, o: int, lse: int, B: int, H: in
     (lse 0: not written); returns the status code."""
     return load_library().attn_fwd_bf16_gqa_ws(q, k, v, o, lse or None, B, H, H_kv, Sq, Sk, layout, round_mode,
                                                mask, workspace or None, workspace_bytes, stream)
+
+
+def attn_fwd_bf16_gqa_noalloc(q: int, k: int, v: int, o: int, lse: int, B: int, H: int, H_kv: int, Sq: int,
+                              Sk: int, layout: int, round_mode: int, mask: int, stream: int) -> int:
+    """attn_fwd_bf16_gqa_ws with the library's static scratch instead of a workspace
+    (allocates nothing; lse 0: not written); returns the status code."""
+    return load_library().attn_fwd_bf16_gqa_noalloc(q, k, v, o, lse or None, B, H, H_kv, Sq, Sk, layout,
+                                                    round_mode, mask, stream)
 
 
 def attn_fwd_bf16_gqa_workspace_size(B: int, H: int, Sq: int, Sk: int, mask: int) -> int:

@@ -95,6 +95,7 @@
 #include <atomic>
 #include <cstdint>
 #include <cstring>
+#include <mutex>
 #include <type_traits>
 
 #include "attn_fwd.h"
@@ -953,6 +954,36 @@ int check_device(int* n_cu) {
   return ok ? ATTN_OK : ATTN_ERR_DEVICE;
 }
 
+// Static scratch of attn_fwd_bf16_gqa_noalloc: the split path's partial rows
+// and (m, l) pairs, for callers that cannot allocate (graph capture, tight
+// serving loops).  Sized for the largest plan on a 256-CU device: 2 x 256
+// partial blocks of BM rows x (D + 2) floats (65 MiB).  Every GPU the library
+// runs on holds its own copy until the process ends; host code reaches it
+// only through the address hipGetSymbolAddress gives for the current device
+// (the array's name on the host is a stand-in, not a device address).
+constexpr int64_t kScratchBytes = int64_t(2) * 256 * BM * (D + 2) * (int64_t)sizeof(float);
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mutex;
+
+// The device address of `scratch` on the current device (looked up once per
+// device, with that device current), or nullptr when the lookup fails.
+void* scratch_address() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  p = g_scratch[dev].load(std::memory_order_relaxed);
+  if (!p) {
+    void* addr = nullptr;
+    if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+    g_scratch[dev].store(addr, std::memory_order_release);
+    p = addr;
+  }
+  return p;
+}
+
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
@@ -1381,9 +1412,12 @@ extern "C" int attn_fwd_bf16_gqa_workspace_size(int64_t B, int64_t H, int64_t Sq
   return ATTN_OK;
 }
 
-extern "C" int attn_fwd_bf16_gqa_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
-                                    int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode,
-                                    int mask, void* workspace, int64_t workspace_bytes, void* stream) {
+namespace {
+// attn_fwd_bf16_gqa_ws, with the workspace given (noalloc false) or the
+// static scratch of the current device (noalloc true)
+int gqa_split_call(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B, int64_t H,
+                   int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode, int mask, void* workspace,
+                   int64_t workspace_bytes, void* stream, bool noalloc) {
   Problem pb;
   const int st = check_args(q, k, v, o, B, H, H_kv, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
@@ -1402,7 +1436,11 @@ extern "C" int attn_fwd_bf16_gqa_ws(const void* q, const void* k, const void* v,
   if (dev_status != ATTN_OK) return dev_status;
   const Plan plan = make_plan_masked(pb.n_work, pb.n_qtiles, Sq, Sk, mask, n_cu);
   const int64_t need = plan_workspace_bytes(plan);
-  if (need > 0) {
+  if (need > 0 && noalloc) {
+    if (need > kScratchBytes) return ATTN_ERR_SCRATCH;
+    workspace = scratch_address();
+    if (!workspace) return ATTN_ERR_HIP;
+  } else if (need > 0) {
     if (!workspace) return ATTN_ERR_NULL;
     if (workspace_bytes < need) return ATTN_ERR_WORKSPACE;
     if ((uintptr_t)workspace & 15) return ATTN_ERR_ALIGN;
@@ -1412,6 +1450,20 @@ extern "C" int attn_fwd_bf16_gqa_ws(const void* q, const void* k, const void* v,
       return ATTN_ERR_ALIAS;
   }
   return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, plan, workspace, stream, nullptr, lse);
+}
+}  // namespace
+
+extern "C" int attn_fwd_bf16_gqa_ws(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
+                                    int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout, int round_mode,
+                                    int mask, void* workspace, int64_t workspace_bytes, void* stream) {
+  return gqa_split_call(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, workspace, workspace_bytes,
+                        stream, false);
+}
+
+extern "C" int attn_fwd_bf16_gqa_noalloc(const void* q, const void* k, const void* v, void* o, float* lse,
+                                         int64_t B, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layout,
+                                         int round_mode, int mask, void* stream) {
+  return gqa_split_call(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, nullptr, 0, stream, true);
 }
 
 extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
@@ -1451,6 +1503,7 @@ extern "C" const char* attn_fwd_bf16_strerror(int status) {
     case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_bf16_workspace_size reports";
     case ATTN_ERR_MASK: return "mask is not an attn_mask_t value";
     case ATTN_ERR_HEADS: return "the query head count is not a multiple of the K/V head count";
+    case ATTN_ERR_SCRATCH: return "the split needs more scratch than the static buffer of attn_fwd_bf16_gqa_noalloc holds";
     default: return "unknown status";
   }
 }

@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define ATTN_FWD_ABI_VERSION 8
+#define ATTN_FWD_ABI_VERSION 9
 
 typedef enum {
     ATTN_LAYOUT_BSHD = 0, /* [B, S, H, 128] */
@@ -79,7 +79,8 @@ typedef enum {
     ATTN_ERR_HIP = 8,    /* the kernel launch failed */
     ATTN_ERR_WORKSPACE = 9, /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
     ATTN_ERR_MASK = 10,     /* mask is not an attn_mask_t value */
-    ATTN_ERR_HEADS = 11     /* H is not a multiple of H_kv */
+    ATTN_ERR_HEADS = 11,    /* H is not a multiple of H_kv */
+    ATTN_ERR_SCRATCH = 12   /* attn_fwd_bf16_gqa_noalloc: the split needs more than its static scratch */
 } attn_status_t;
 
 /*
@@ -274,6 +275,30 @@ int attn_fwd_bf16_gqa_ws(const void *q, const void *k, const void *v, void *o,
                          float *lse, int64_t B, int64_t H, int64_t H_kv, int64_t Sq,
                          int64_t Sk, int layout, int round_mode, int mask,
                          void *workspace, int64_t workspace_bytes, void *stream);
+
+/*
+ * attn_fwd_bf16_gqa_noalloc -- attn_fwd_bf16_gqa_ws without a workspace
+ * argument, for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * The key-range split keeps its partial rows and (maximum, sum) pairs in a
+ * static device array of the library (65 MiB, enough for every split plan
+ * on a device of up to 256 compute units: 2 x 256 blocks of 256 rows x 130
+ * floats), one per device, held from the library's load until the process
+ * ends.  The call allocates and frees nothing.  Every call on a device
+ * shares that device's array: calls that may overlap on one device (on
+ * different streams, or from different threads) race and must be ordered by
+ * the caller.  Nothing in the array has to start at zero: each call writes
+ * every partial it reads.
+ *
+ * Arguments, results and status codes as attn_fwd_bf16_gqa_ws (the same
+ * plan, kernels and bits), without workspace and workspace_bytes; a plan
+ * that needs more than the static array returns ATTN_ERR_SCRATCH and
+ * launches nothing.
+ */
+int attn_fwd_bf16_gqa_noalloc(const void *q, const void *k, const void *v, void *o,
+                              float *lse, int64_t B, int64_t H, int64_t H_kv, int64_t Sq,
+                              int64_t Sk, int layout, int round_mode, int mask, void *stream);
 
 /*
  * attn_fwd_bf16_gqa_workspace_size -- bytes of workspace attn_fwd_bf16_gqa_ws

@@ -45,9 +45,11 @@ int main() {
         ATTN_ERR_ALIGN);
   CHECK(attn_fwd_bf16_gqa(q, k, v, o, static_cast<float*>(q), 1, 4, 2, 1, 1, 0, 0, 0, nullptr) == ATTN_ERR_ALIAS);
   CHECK(attn_fwd_bf16_gqa(q, k, v, o, lse, 1, 4, 2, 1, 1, 0, 0, 1, nullptr) == ATTN_ERR_DEVICE);
-  // workspace variants
+  // workspace and static-scratch variants
   CHECK(attn_fwd_bf16_ws(q, k, v, o, 1, 1, 1, 1, 0, 0, ws, -1, nullptr) == ATTN_ERR_SIZE);
   CHECK(attn_fwd_bf16_gqa_ws(q, k, v, o, lse, 1, 4, 2, 1, 1, 0, 0, 3, ws, 16, nullptr) == ATTN_ERR_MASK);
+  CHECK(attn_fwd_bf16_gqa_noalloc(q, k, v, o, lse, 1, 4, 2, 1, 1, 0, 0, 3, nullptr) == ATTN_ERR_MASK);
+  CHECK(attn_fwd_bf16_gqa_noalloc(q, k, v, o, lse, 1, 4, 2, 1, 1, 0, 0, 2, nullptr) == ATTN_ERR_DEVICE);
   int64_t bytes = -1;
   CHECK(attn_fwd_bf16_workspace_size(1, 1, 1, 1, nullptr) == ATTN_ERR_NULL);
   CHECK(attn_fwd_bf16_workspace_size(0, 1, 1, 1, &bytes) == ATTN_ERR_SIZE && bytes == 0);

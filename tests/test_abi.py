@@ -25,8 +25,8 @@ def _enum_values():
 
 def test_library_exports_every_declared_symbol():
     funcs = _declared_functions()
-    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_gqa_workspace_size",
-                     "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_masked", "attn_fwd_bf16_merge", "attn_fwd_bf16_partial",
+    assert funcs == ["attn_fwd_bf16", "attn_fwd_bf16_abi_version", "attn_fwd_bf16_gqa", "attn_fwd_bf16_gqa_noalloc",
+                     "attn_fwd_bf16_gqa_workspace_size", "attn_fwd_bf16_gqa_ws", "attn_fwd_bf16_masked", "attn_fwd_bf16_merge", "attn_fwd_bf16_partial",
                      "attn_fwd_bf16_split_plan", "attn_fwd_bf16_split_plan_masked", "attn_fwd_bf16_strerror",
                      "attn_fwd_bf16_varlen",
                      "attn_fwd_bf16_workspace_size", "attn_fwd_bf16_ws"]
@@ -269,6 +269,21 @@ W_ = 0x70000  # a fake workspace
 def test_gqa_ws_argument_errors_before_any_hip_call(args, code):
     ev = _enum_values()
     assert attn.attn_fwd_bf16_gqa_ws(*args, 0) == ev[code]
+
+
+@pytest.mark.parametrize("args,code", [
+    ((0, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 0, 1), "ATTN_ERR_NULL"),
+    ((A, B_, C, O_, 0, 1, 4, 3, 1, 1, 0, 0, 1), "ATTN_ERR_HEADS"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 0, 1, 0, 0, 1), "ATTN_ERR_SIZE"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 2, 0, 1), "ATTN_ERR_LAYOUT"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 3, 1), "ATTN_ERR_ROUND"),
+    ((A, B_, C, O_, L_ + 1, 1, 4, 2, 1, 1, 0, 0, 1), "ATTN_ERR_ALIGN"),
+    ((A, B_, C, O_, O_, 1, 4, 2, 1, 1, 0, 0, 1), "ATTN_ERR_ALIAS"),
+    ((A, B_, C, O_, 0, 1, 4, 2, 1, 1, 0, 0, 3), "ATTN_ERR_MASK"),
+])
+def test_gqa_noalloc_argument_errors_before_any_hip_call(args, code):
+    ev = _enum_values()
+    assert attn.attn_fwd_bf16_gqa_noalloc(*args, 0) == ev[code]
 
 
 def test_gqa_workspace_size_argument_errors():
