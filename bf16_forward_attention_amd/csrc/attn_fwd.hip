@@ -264,32 +264,17 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
 // In every instantiation a wave whose 32 rows all lie past Sq (the ragged
 // last q-tile) skips the products and only loads.
 template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN>
-__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
-    uint16_t* __restrict__ O, int H, int Sq_all, int Sk_all, int n_qtiles, Geometry g, Split sp, Varlen vl,
-    int causal_br, int64_t causal_off_fixed, float* __restrict__ lse) {
+__device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                                          const uint16_t* __restrict__ V, uint16_t* __restrict__ O, int H,
+                                          int Sq_all, int Sk_all, int n_qtiles, const Geometry& g, const Split& sp,
+                                          const Varlen& vl, int causal_br, int64_t causal_off_fixed,
+                                          float* __restrict__ lse, uint8_t* lds, int work, int t_begin, int t_end,
+                                          int slot) {
   // K stages in the lower 64 KiB, V stages in the upper 64 KiB
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
   uint8_t* const k_st[NSTAGE] = {lds, lds + TILE_BYTES, lds + 2 * TILE_BYTES, lds + 3 * TILE_BYTES};
   uint8_t* const v_st[NSTAGE] = {lds + 4 * TILE_BYTES, lds + 5 * TILE_BYTES, lds + 6 * TILE_BYTES,
                                  lds + 7 * TILE_BYTES};
-
-  // ---- workgroup -> (b, h, q-tile) and key-tile range ----
-  // Whole items: workgroups are dispatched round-robin over the 8 XCDs;
-  // renumber so that XCD x receives a contiguous range of logical work items
-  // (a head's q-tiles share one XCD's L2).  Split items follow in id order.
   const int id = blockIdx.x;
-  int work, t_begin = 0, t_end = (Sk_all + BN - 1) / BN, slot = -1;
-  if (!SPLIT || id < sp.n_whole) {
-    const int xcd = id & 7, local = id >> 3;
-    const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
-    work = xcd * per + (xcd < rem ? xcd : rem) + local;
-  } else {
-    slot = id - sp.n_whole;
-    work = split_item_work(sp, slot / sp.splits, n_qtiles);
-    t_begin = (slot % sp.splits) * sp.tiles_per_split;
-    t_end = t_begin + sp.tiles_per_split < t_end ? t_begin + sp.tiles_per_split : t_end;
-  }
   // causal: a head's q-tiles in decreasing order, the ones with the most
   // visible keys dispatched first
   int qt = CAUSAL ? n_qtiles - 1 - work % n_qtiles : work % n_qtiles;
@@ -829,6 +814,59 @@ __global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
   }
 }
 
+// Work decomposition.  Whole items: workgroups are dispatched round-robin
+// over the 8 XCDs; they are renumbered so that XCD x receives a contiguous
+// range of logical work items (a head's q-tiles share one XCD's L2).  Split
+// items follow in id order.
+// PAIRS (causal mask, fixed-length batches, whole items only): each
+// workgroup runs two work items of one head one after the other, q-tiles
+// n-1-j and j, so every workgroup sees about the same number of key tiles
+// and there are half as many workgroups to start and finish (the hardware
+// dispatcher's balancing works on the workgroups as before).  An odd q-tile
+// count leaves the middle q-tile of a head alone.  Pairs are numbered over
+// the heads (sp.n_whole = their count) and renumbered per XCD like items.
+template <int MODE, bool SPLIT, bool CAUSAL, bool VARLEN, bool PAIRS>
+__global__ __launch_bounds__(NTHREADS, 1) void attn_fwd_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    uint16_t* __restrict__ O, int H, int Sq_all, int Sk_all, int n_qtiles, Geometry g, Split sp, Varlen vl,
+    int causal_br, int64_t causal_off_fixed, float* __restrict__ lse) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[2 * NSTAGE * TILE_BYTES];
+  const int id = blockIdx.x;
+  const int n_tiles_all = (Sk_all + BN - 1) / BN;
+  if constexpr (PAIRS) {
+    const int xcd = id & 7, local = id >> 3;
+    const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
+    const int pair = xcd * per + (xcd < rem ? xcd : rem) + local;
+    const int per_head = (n_qtiles + 1) >> 1;
+    const int head = pair / per_head, j = pair % per_head;
+    // work items (see attn_item: under a causal mask item w is q-tile n-1-(w % n))
+    const int wa = head * n_qtiles + j, wb = head * n_qtiles + n_qtiles - 1 - j;
+    const int n_items = n_qtiles - 1 - j != j ? 2 : 1;
+    attn_item<MODE, SPLIT, CAUSAL, VARLEN>(Q, K, V, O, H, Sq_all, Sk_all, n_qtiles, g, sp, vl, causal_br,
+                                           causal_off_fixed, lse, lds, wa, 0, n_tiles_all, -1);
+    if (n_items == 2) {
+      // the first item's waves are done with the LDS stages the second one fills
+      __syncthreads();
+      attn_item<MODE, SPLIT, CAUSAL, VARLEN>(Q, K, V, O, H, Sq_all, Sk_all, n_qtiles, g, sp, vl, causal_br,
+                                             causal_off_fixed, lse, lds, wb, 0, n_tiles_all, -1);
+    }
+  } else {
+    int work, t_begin = 0, t_end = n_tiles_all, slot = -1;
+    if (!SPLIT || id < sp.n_whole) {
+      const int xcd = id & 7, local = id >> 3;
+      const int per = sp.n_whole >> 3, rem = sp.n_whole & 7;
+      work = xcd * per + (xcd < rem ? xcd : rem) + local;
+    } else {
+      slot = id - sp.n_whole;
+      work = split_item_work(sp, slot / sp.splits, n_qtiles);
+      t_begin = (slot % sp.splits) * sp.tiles_per_split;
+      t_end = t_begin + sp.tiles_per_split < t_end ? t_begin + sp.tiles_per_split : t_end;
+    }
+    attn_item<MODE, SPLIT, CAUSAL, VARLEN>(Q, K, V, O, H, Sq_all, Sk_all, n_qtiles, g, sp, vl, causal_br,
+                                           causal_off_fixed, lse, lds, work, t_begin, t_end, slot);
+  }
+}
+
 // Combines the key-range partials of the split work items: per query row,
 // M = max_s m_s, w_s = 2^(m_s - M), O = (sum_s w_s o_s) * (1 / sum_s w_s l_s),
 // summed in split order, then the one rounding to bf16.  One thread per
@@ -1107,28 +1145,36 @@ Geometry make_geometry(int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layo
 template <int MODE>
 void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
             int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg, int n_split_items,
-            int mask, float* lse, hipStream_t s) {
+            int mask, float* lse, bool pairs, hipStream_t s) {
   const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
   const int64_t off = br ? (int64_t)Sk - Sq : 0;  // fixed-length calls: row i sees keys j <= i + off
   const Varlen none{nullptr, nullptr, 0, 0, 0};
   const dim3 grid((unsigned)n_wg), block(NTHREADS);
+  if (pairs) {
+    // two work items per workgroup (fixed-length, no split): n_wg counts the pairs
+    Split spp = sp;
+    spp.n_whole = (int)n_wg;
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+                       n_qtiles, g, spp, none, 0, off, lse);
+    return;
+  }
   if (n_split_items > 0 && mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, none, 0, off, lse);
   else if (n_split_items > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, none, 0, (int64_t)0, lse);
   else if (vl && mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, *vl, br, (int64_t)0, lse);
   else if (vl)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, *vl, 0, (int64_t)0, lse);
   else if (mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, none, 0, off, lse);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
+    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
                        n_qtiles, g, sp, none, 0, (int64_t)0, lse);
   if (n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
@@ -1139,14 +1185,19 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
 
 int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
         int layout, int round_mode, int mask, const Problem& pb, const Plan& plan, void* workspace, void* stream,
-        const Varlen* vl = nullptr, float* lse = nullptr) {
+        int n_cu, const Varlen* vl = nullptr, float* lse = nullptr) {
   const Geometry g = make_geometry(H, H_kv, Sq, Sk, layout);
   Split sp{(int)plan.n_whole, (int)plan.splits, (int)plan.tiles_per_split, nullptr, nullptr, (int)plan.qt_major};
   if (plan.n_split_items > 0) {
     sp.part = (float*)workspace;
     sp.ml = sp.part + plan.n_split_items * plan.splits * BM * D;
   }
-  const int64_t n_wg = plan.n_whole + plan.n_split_items * plan.splits;
+  int64_t n_wg = plan.n_whole + plan.n_split_items * plan.splits;
+  // causal whole fixed-length items in at least two rounds of compute units: two per workgroup
+  // (without a mask the items are equal already, and one per workgroup measured faster)
+  const bool pairs =
+      mask != ATTN_MASK_NONE && !vl && plan.n_split_items == 0 && n_cu > 0 && pb.n_work >= 2 * (int64_t)n_cu;
+  if (pairs) n_wg = pb.n_work / pb.n_qtiles * ((pb.n_qtiles + 1) / 2);
   const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
   uint16_t* oo = (uint16_t*)o;
   hipStream_t s = (hipStream_t)stream;
@@ -1154,15 +1205,15 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
       launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, s);
+                             mask, lse, pairs, s);
       break;
     case ATTN_ROUND_RTNA:
       launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, s);
+                             mask, lse, pairs, s);
       break;
     default:
       launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, s);
+                             mask, lse, pairs, s);
       break;
   }
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
@@ -1179,7 +1230,7 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream);
+  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream, n_cu);
 }
 
 extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, void* o, float* lse, int64_t B,
@@ -1202,7 +1253,7 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
   const int dev_status = check_device(&n_cu);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
-  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream, nullptr, lse);
+  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream, n_cu, nullptr, lse);
 }
 
 extern "C" int attn_fwd_bf16_masked(const void* q, const void* k, const void* v, void* o, int64_t B, int64_t H,
@@ -1260,7 +1311,7 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
   pb.n_work = n_wg;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
   return run(q, k, v, o, H, H_kv, max_seqlen_q, 1, ATTN_LAYOUT_BSHD, round_mode, mask, pb, whole, nullptr, stream,
-             &vl, lse);
+             n_cu, &vl, lse);
 }
 
 extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v, float* o_part, float* lse_part,
@@ -1296,10 +1347,10 @@ extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v
   uint16_t* oo = (uint16_t*)o_part;
   hipStream_t s = (hipStream_t)stream;
   if (mask == ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
+    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, false, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
                        (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, (int64_t)0, lse_part);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, true, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
+    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, true, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
                        (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, off, lse_part);
   return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
@@ -1449,7 +1500,8 @@ int gqa_split_call(const void* q, const void* k, const void* v, void* o, float* 
         (lse && overlaps(workspace, need, lse, pb.bytes_q / 64)))
       return ATTN_ERR_ALIAS;
   }
-  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, plan, workspace, stream, nullptr, lse);
+  return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, plan, workspace, stream, n_cu, nullptr,
+             lse);
 }
 }  // namespace
 
@@ -1486,7 +1538,7 @@ extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, voi
         overlaps(workspace, need, v, pb.bytes_k) || overlaps(workspace, need, o, pb.bytes_q))
       return ATTN_ERR_ALIAS;
   }
-  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, plan, workspace, stream);
+  return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, plan, workspace, stream, n_cu);
 }
 
 extern "C" const char* attn_fwd_bf16_strerror(int status) {

@@ -93,3 +93,44 @@ def test_none_mask_matches_unmasked_entry_point():
         launch_masked(dev.q, dev.k, dev.v, dev.o, "bshd", mode, "none")
         torch.cuda.synchronize()
         assert np.array_equal(to_bits(dev.o), want), mode
+
+
+@pytest.mark.parametrize("mask", MASKS)
+@pytest.mark.parametrize("shape", [(2, 37, 37, 1700, 1700, "bshd"), (1, 74, 37, 1700, 1900, "bhsd"),
+                                   (1, 64, 16, 2048, 1500, "bshd")],
+                         ids=["odd_qtiles", "odd_qtiles_gqa_longer_keys", "even_qtiles_gqa_shorter_keys"])
+def test_paired_workgroups(shape, mask):
+    # enough causal work items for two rounds of compute units: each workgroup runs q-tiles n-1-j and j
+    # of a head one after the other (7 q-tiles per head leave the middle one alone); every row against
+    # the oracle, and the lse of the rows of both items of a workgroup
+    from tests.gate import lse_gate, lse_tolerance
+    from tests.gpu_util import launch_gqa, to_device
+    B, H, H_kv, Sq, Sk, layout = shape
+    n_qtiles = -(-Sq // 256)
+    assert B * H * n_qtiles >= 2 * torch.cuda.get_device_properties(0).multi_processor_count
+    inp = synth.small(B, H, Sq, Sk, layout, seed=Sq + H, mask=mask, H_kv=H_kv)
+    ex, rd, ls = oracle.attn_rows(inp.q, inp.k, inp.v, layout,
+                                  [(b, h, i) for b in range(B) for h in range(H) for i in range(Sq)],
+                                  mask=mask, with_lse=True)
+    ex = ex.reshape(B, H, Sq, 128)
+    rd = rd.reshape(B, H, Sq, 3, 128)
+    ls = ls.reshape(B, H, Sq)
+    q, k, v = to_device(inp.q), to_device(inp.k), to_device(inp.v)
+    o = torch.empty_like(q)
+    lse = torch.empty((B, H, Sq), dtype=torch.float32, device="cuda:0")
+    for m, mode in enumerate(MODES):
+        launch_gqa(q, k, v, o, layout, mode, mask, lse=lse)
+        torch.cuda.synchronize()
+        got = np.ascontiguousarray(synth.to_logical(to_bits(o), layout))
+        res = gate(got, rd[:, :, :, m], ex)
+        say(f"  {shape} {mask} {mode}: {res.summary()}")
+        assert res.ok, (mode, res.summary())
+    # lse against the oracle's, within the bound derived from the fp32 arithmetic
+    from tests.test_gpu_lse import _bound_inputs
+    ql, kl = synth.to_logical(inp.q, layout), synth.to_logical(inp.k, layout)
+    got = lse.cpu().numpy()
+    for b in range(B):
+        dmax, nvis = _bound_inputs(ql[b:b + 1], kl[b:b + 1], mask, Sq, Sk)
+        ok, worst, n = lse_gate(got[b:b + 1], ls[b:b + 1], lse_tolerance(dmax, nvis, ls[b:b + 1]))
+        say(f"  lse batch {b}: worst {worst:.3f} of the bound over {n} rows")
+        assert ok, worst

@@ -31,7 +31,7 @@ def _bound_inputs(q_log, k_log, mask, Sq, Sk):
     H, H_kv = q_log.shape[1], k_log.shape[1]
     qa = np.abs(cases.val(q_log))
     ka = np.repeat(np.abs(cases.val(k_log)), H // H_kv, axis=1)
-    dots = np.einsum("bhid,bhjd->bhij", qa, ka) / math.sqrt(128)
+    dots = np.matmul(qa, np.ascontiguousarray(np.swapaxes(ka, -1, -2))) / math.sqrt(128)
     i = np.arange(Sq)[:, None]
     j = np.arange(Sk)[None, :]
     if mask == "none":
