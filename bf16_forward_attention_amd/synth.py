@@ -228,6 +228,7 @@ class Workload:
     seed: int = 0
     mask: str = "none"  # key mask the workload is run with: "none", "causal", "causal_br"
     H_kv: int = 0  # K/V heads (grouped-query attention); 0: as many as query heads
+    zero_kv: bool = False  # K and V all +0 (Q as drawn): same work, operands that barely toggle
 
     @property
     def kv_heads(self) -> int:
@@ -256,6 +257,10 @@ WORKLOADS = {
     "gqa8k_causal": Workload("gqa8k_causal", 2, 32, 8192, 8192, "bshd", ("rtne",), mask="causal", H_kv=8),
     # one long causal sequence over few heads: 256 work items of 4 .. 256 key tiles, a single round
     "causal16k_4h": Workload("causal16k_4h", 1, 4, 16384, 16384, "bshd", ("rtne",), mask="causal"),
+    # a power diagnostic: the self8k shapes and instruction stream with K = V = 0 (every logit 0,
+    # every output row exactly 0), so the matrix cores multiply zeros; set against self8k it shows
+    # how much of the board power the arithmetic on random data draws
+    "self8k_zero_kv": Workload("self8k_zero_kv", 4, 16, 8192, 8192, "bshd", ("rtne",), zero_kv=True),
 }
 
 
@@ -316,6 +321,10 @@ def generate(wl: Workload) -> Inputs:
     nq = wl.B * wl.H * wl.Sq * D
     nk = wl.B * wl.kv_heads * wl.Sk * D
     q = normal_bf16(wl.seed, TID_Q, nq, wl.qk_sigma).reshape(wl.B, wl.H, wl.Sq, D)
+    if wl.zero_kv:
+        k = np.zeros((wl.B, wl.kv_heads, wl.Sk, D), dtype=np.uint16)
+        v = np.zeros((wl.B, wl.kv_heads, wl.Sk, D), dtype=np.uint16)
+        return Inputs(wl, to_layout(q, wl.layout), to_layout(k, wl.layout), to_layout(v, wl.layout), [], [])
     k = normal_bf16(wl.seed, TID_K, nk, wl.qk_sigma).reshape(wl.B, wl.kv_heads, wl.Sk, D)
     if wl.v_dist == "normal":
         v = normal_bf16(wl.seed, TID_V, nk, 1.0)

@@ -103,3 +103,16 @@ def test_checked_rows_subset():
     for h in range(3):
         idx = [r[2] for r in rows if r[1] == h]
         assert len(set(idx)) == 64 and max(idx) < 5000
+
+
+def test_zero_kv_workload_keeps_q_and_zeroes_k_and_v():
+    wl = synth.Workload("t", 2, 3, 70, 90, "bshd", ("rtne",), zero_kv=True)
+    plain = synth.Workload("t", 2, 3, 70, 90, "bshd", ("rtne",))
+    z, p = synth.generate(wl), synth.generate(plain)
+    assert np.array_equal(z.q, p.q)
+    assert z.k.shape == p.k.shape and z.v.shape == p.v.shape
+    assert not z.k.any() and not z.v.any()
+    assert synth.WORKLOADS["self8k_zero_kv"].zero_kv
+    base, diag = synth.WORKLOADS["self8k"], synth.WORKLOADS["self8k_zero_kv"]
+    assert (diag.B, diag.H, diag.Sq, diag.Sk, diag.layout, diag.modes) == \
+        (base.B, base.H, base.Sq, base.Sk, base.layout, base.modes)
