@@ -24,8 +24,12 @@ BSHD, RTNE.  Prints one JSON line:
   sweep      (with the default workload, or --sweep; under rocprofv3 only with --sweep)
              the other configurations of 8K and longer, each timed alone the same way
              after the headline: the 128K long-context workload in all three rounding
-             modes, the 4097 x 32771 cross-attention and the stressed 32760 x 32760 workload, each with its
-             rate, share of the peak, clock and a parity sample against the oracle
+             modes, the 4097 x 32771 cross-attention and the stressed 32760 x 32760
+             workload, each with its rate, share of the peak, clock and a parity sample
+             against the oracle
+  power_reference  (with the sweep) the headline's shapes and instructions on K = V = 0,
+             timed the same way: not a benchmark workload, a reference for how far the
+             arithmetic on random data lowers the clock under the power limit
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
        [--mode rtne|rtna|rtz] [--no-cpu-baseline] [--cpu-seconds S] [--no-split] [--no-clock]
@@ -399,6 +403,12 @@ def time_launches(step, stream, steps):
 # lengths and the stressed diffusion-transformer-like workload.
 SWEEP = (("long128k", "rtne"), ("long128k", "rtna"), ("long128k", "rtz"), ("cross_odd", "rtz"),
          ("dit_stress", "rtna"))
+# timed after the sweep and reported apart from it: the headline's shapes and instructions on zero K and V,
+# a reference for how much the arithmetic on random data lowers the clock under the power limit
+POWER_REFERENCE = (("self8k_zero_kv", "rtne"),)
+POWER_REFERENCE_NOTE = ("not a benchmark workload: self8k with K = V = 0 (every output 0), the same "
+                        "instructions on operands that barely switch; set its clock and rate against "
+                        "the headline's")
 
 
 def sweep_parity_rows(inp, n=128):
@@ -426,9 +436,10 @@ def sweep_parity_rows(inp, n=128):
     return sorted(rows)
 
 
-def run_sweep(args, dev):
-    """Time each SWEEP configuration on its own (inputs resident, the same launch protocol as the
-    headline), with the clock under it and a parity sample of its output against the oracle."""
+def run_sweep(args, dev, configs=SWEEP):
+    """Time each configuration of ``configs`` on its own (inputs resident, the same launch protocol
+    as the headline), with the clock under it and a parity sample of its output against the
+    oracle."""
     import torch
 
     import bf16_forward_attention_amd as attn
@@ -439,7 +450,7 @@ def run_sweep(args, dev):
     stream = torch.cuda.current_stream(dev)
     out = []
     loaded = None
-    for name, mode in SWEEP:
+    for name, mode in configs:
         wl = synth.WORKLOADS[name]
         if loaded is None or loaded[0].wl.name != name:
             loaded = None
@@ -600,6 +611,7 @@ def main():
     if args.sweep or (args.sweep is None and args.workload == "self8k" and not under_profiler()):
         del q, k, v, o, ws, step
         result["sweep"] = run_sweep(args, dev)
+        result["power_reference"] = {"note": POWER_REFERENCE_NOTE, "runs": run_sweep(args, dev, POWER_REFERENCE)}
     print(json.dumps(result), flush=True)
 
 

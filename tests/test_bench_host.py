@@ -150,3 +150,11 @@ def test_sweep_parity_rows():
     for _, b, h, _, _ in inp.specials:
         assert sum(1 for r in rows if r[:2] == (b, h)) >= 8
     assert all(0 <= i < wl.Sq for _, _, i in rows)
+
+
+def test_power_reference_is_the_headline_on_zero_operands():
+    assert len(bench.POWER_REFERENCE) == 1
+    name, mode = bench.POWER_REFERENCE[0]
+    wl, head = synth.WORKLOADS[name], synth.WORKLOADS["self8k"]
+    assert wl.zero_kv and mode in wl.modes and (name, mode) not in bench.SWEEP
+    assert (wl.B, wl.H, wl.Sq, wl.Sk, wl.layout, wl.mask) == (head.B, head.H, head.Sq, head.Sk, head.layout, head.mask)
