@@ -271,3 +271,24 @@ def test_varlen_mix_causal():
     res = gate(got, rd[:, 0], ex)
     say(f"  varlen_mix rtne: {res.summary()}")
     assert res.ok, res.summary()
+
+
+@pytest.mark.timeout(600)
+def test_zero_keys_and_values_give_exact_zeros():
+    # self8k's shapes and Q with K = V = +0 (the bench's power reference): every logit is 0 and
+    # every output a mean of zero rows, +0 in every mode by the definition. Every element of the
+    # unmasked, causal and split outputs must be +0, and sampled rows must match the oracle's bits.
+    wl = synth.WORKLOADS["self8k_zero_kv"]
+    inp = synth.generate(wl)
+    rows = _rows_for(wl, n_random=64)
+    ex, rd = oracle.attn_rows(inp.q, inp.k, inp.v, wl.layout, rows, mask="none")
+    assert not np.any(rd) and not np.any(ex)
+    dev = Dev(inp)
+    for mode in MODES:
+        for kind, out in (("single", dev.run(mode)), ("causal", dev.run(mode, mask="causal")),
+                          ("split", dev.run(mode, split=True))):
+            nonzero = int(np.count_nonzero(out))
+            say(f"  self8k_zero_kv {mode} {kind}: {nonzero} nonzero elements")
+            assert nonzero == 0, f"{mode} {kind}: {nonzero} elements are not +0"
+            res = gate(_gather(out, wl.layout, rows), rd[:, MODES.index(mode)], ex)
+            assert res.ok and res.max_row_ulps == 0, f"{mode} {kind}: {res.summary()}"
