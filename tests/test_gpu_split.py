@@ -139,3 +139,43 @@ def test_workspace_errors_on_device():
     assert attn.attn_fwd_bf16_ws(*args, dq.data_ptr(), need, s) == 6  # ATTN_ERR_ALIAS (workspace over q)
     assert attn.attn_fwd_bf16_ws(*args, ws.data_ptr(), need, s) == 0
     torch.cuda.synchronize()
+
+
+# decode-like shapes: a few query rows against a long key cache. They leave most compute units
+# idle, so the splitting entry points cut the keys into ranges; each shape is checked single pass
+# and split, unmasked in every mode, and with the bottom-right causal mask (each new query sees
+# the cache and the new keys up to its own position) through attn_fwd_bf16_gqa_ws.
+DECODE_SHAPES = [(1, 8, 1, 131072), (2, 4, 16, 65537), (1, 16, 7, 40000)]
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("shape", DECODE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_decode_like_long_key_caches(shape):
+    B, H, Sq, Sk = shape
+    assert attn.attn_fwd_bf16_workspace_size(B, H, Sq, Sk) > 0, "shape expected to split"
+    inp = synth.small(B, H, Sq, Sk, "bshd", seed=Sk + Sq)
+    ex, rd = oracle.attn_all(inp.q, inp.k, inp.v, "bshd")
+    dev = Dev(inp)
+    for split in (False, True):
+        for m, mode in enumerate(MODES):
+            res = gate(dev.run_logical(mode, split=split), rd[m], ex)
+            say(f"  decode {shape} split={split} {mode}: {res.summary()}")
+            assert res.ok, res.summary()
+    ex, rd = oracle.attn_all(inp.q, inp.k, inp.v, "bshd", mask="causal_br")
+    for split in (False, True):
+        res = gate(dev.run_logical("rtna", split=split, mask="causal_br"), rd[1], ex)
+        say(f"  decode {shape} causal_br split={split} rtna: {res.summary()}")
+        assert res.ok, res.summary()
+
+
+@pytest.mark.timeout(300)
+def test_one_key_against_many_query_rows():
+    # every row's only weight is exp2(<= 0) rounded to 1, so every output row is V's one row,
+    # bit for bit, in every mode; 70001 rows over two heads (274 work items, a ragged last q-tile)
+    inp = synth.small(1, 2, 70001, 1, "bhsd", seed=77)
+    dev = Dev(inp)
+    v = synth.to_logical(inp.v, "bhsd")
+    for mode in MODES:
+        got = dev.run_logical(mode, split=True)
+        for h in range(2):
+            assert np.array_equal(got[0, h], np.broadcast_to(v[0, h, 0], got[0, h].shape)), (mode, h)
