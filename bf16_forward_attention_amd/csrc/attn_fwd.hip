@@ -96,7 +96,9 @@
 #include <cstdint>
 #include <cstring>
 #include <mutex>
+#include <tuple>
 #include <type_traits>
+#include <utility>
 
 #include "attn_fwd.h"
 
@@ -1024,6 +1026,22 @@ void* scratch_address() {
 
 bool mul_ok(int64_t a, int64_t b, int64_t* out) { return !__builtin_mul_overflow(a, b, out); }
 
+// Launch kern on stream s and return that launch's own status: hipGetLastError
+// would also report (and clear) an error that an earlier call of the caller
+// left behind.  The arguments are converted to the kernel's parameter types
+// and passed by address, one pointer per parameter.
+template <typename K, typename T, size_t... I>
+hipError_t launch_args(K kern, dim3 grid, dim3 block, hipStream_t s, T& args, std::index_sequence<I...>) {
+  void* ptrs[] = {(void*)&std::get<I>(args)...};
+  return hipLaunchKernel((const void*)kern, grid, block, ptrs, 0, s);
+}
+template <typename... P, typename... A>
+hipError_t launch_kernel(void (*kern)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<P...> args(std::forward<A>(a)...);
+  return launch_args(kern, grid, block, s, args, std::index_sequence_for<P...>{});
+}
+
 bool overlaps(const void* a, int64_t na, const void* b, int64_t nb) {
   const uintptr_t x = (uintptr_t)a, y = (uintptr_t)b;
   return x < y + (uintptr_t)nb && y < x + (uintptr_t)na;
@@ -1143,9 +1161,9 @@ Geometry make_geometry(int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk, int layo
 }
 
 template <int MODE>
-void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
-            int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg, int n_split_items,
-            int mask, float* lse, bool pairs, hipStream_t s) {
+hipError_t launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o, int H, int Sq, int Sk,
+                  int n_qtiles, const Geometry& g, const Split& sp, const Varlen* vl, int64_t n_wg,
+                  int n_split_items, int mask, float* lse, bool pairs, hipStream_t s) {
   const int br = mask == ATTN_MASK_CAUSAL_BOTTOM_RIGHT;
   const int64_t off = br ? (int64_t)Sk - Sq : 0;  // fixed-length calls: row i sees keys j <= i + off
   const Varlen none{nullptr, nullptr, 0, 0, 0};
@@ -1154,33 +1172,34 @@ void launch(const uint16_t* q, const uint16_t* k, const uint16_t* v, uint16_t* o
     // two work items per workgroup (fixed-length, no split): n_wg counts the pairs
     Split spp = sp;
     spp.n_whole = (int)n_wg;
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false, true>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, spp, none, 0, off, lse);
-    return;
+    return launch_kernel(attn_fwd_kernel<MODE, false, true, false, true>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                         n_qtiles, g, spp, none, 0, off, lse);
   }
+  hipError_t e;
   if (n_split_items > 0 && mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, off, lse);
+    e = launch_kernel(attn_fwd_kernel<MODE, true, true, false, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, none, 0, off, lse);
   else if (n_split_items > 0)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, true, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, (int64_t)0, lse);
+    e = launch_kernel(attn_fwd_kernel<MODE, true, false, false, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, none, 0, (int64_t)0, lse);
   else if (vl && mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, br, (int64_t)0, lse);
+    e = launch_kernel(attn_fwd_kernel<MODE, false, true, true, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, *vl, br, (int64_t)0, lse);
   else if (vl)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, true, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, *vl, 0, (int64_t)0, lse);
+    e = launch_kernel(attn_fwd_kernel<MODE, false, false, true, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, *vl, 0, (int64_t)0, lse);
   else if (mask != ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, true, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, off, lse);
+    e = launch_kernel(attn_fwd_kernel<MODE, false, true, false, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, none, 0, off, lse);
   else
-    hipLaunchKernelGGL((attn_fwd_kernel<MODE, false, false, false, false>), grid, block, 0, s, q, k, v, o, H, Sq, Sk,
-                       n_qtiles, g, sp, none, 0, (int64_t)0, lse);
-  if (n_split_items > 0) {
+    e = launch_kernel(attn_fwd_kernel<MODE, false, false, false, false>, grid, block, s, q, k, v, o, H, Sq, Sk,
+                      n_qtiles, g, sp, none, 0, (int64_t)0, lse);
+  if (e == hipSuccess && n_split_items > 0) {
     const int64_t threads = (int64_t)n_split_items * BM * (D / 4);
-    hipLaunchKernelGGL(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, s, o, H,
-                       Sq, n_qtiles, g, sp, n_split_items, mask != ATTN_MASK_NONE ? 1 : 0, lse);
+    e = launch_kernel(attn_merge_kernel<MODE>, dim3((unsigned)((threads + 255) / 256)), dim3(256), s, o, H, Sq,
+                      n_qtiles, g, sp, n_split_items, mask != ATTN_MASK_NONE ? 1 : 0, lse);
   }
+  return e;
 }
 
 int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t H_kv, int64_t Sq, int64_t Sk,
@@ -1202,21 +1221,22 @@ int run(const void* q, const void* k, const void* v, void* o, int64_t H, int64_t
   uint16_t* oo = (uint16_t*)o;
   hipStream_t s = (hipStream_t)stream;
   const int nsi = (int)plan.n_split_items;
+  hipError_t e;
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
-      launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, pairs, s);
+      e = launch<ATTN_ROUND_RTNE>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                                  mask, lse, pairs, s);
       break;
     case ATTN_ROUND_RTNA:
-      launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, pairs, s);
+      e = launch<ATTN_ROUND_RTNA>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                                  mask, lse, pairs, s);
       break;
     default:
-      launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
-                             mask, lse, pairs, s);
+      e = launch<ATTN_ROUND_RTZ>(qq, kk, vv, oo, (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, vl, n_wg, nsi,
+                                 mask, lse, pairs, s);
       break;
   }
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 }  // namespace
@@ -1346,13 +1366,13 @@ extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v
   const uint16_t *qq = (const uint16_t*)q, *kk = (const uint16_t*)k, *vv = (const uint16_t*)v;
   uint16_t* oo = (uint16_t*)o_part;
   hipStream_t s = (hipStream_t)stream;
-  if (mask == ATTN_MASK_NONE)
-    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, false, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
-                       (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, (int64_t)0, lse_part);
-  else
-    hipLaunchKernelGGL((attn_fwd_kernel<kPartial, false, true, false, false>), grid, block, 0, s, qq, kk, vv, oo, (int)H,
-                       (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, off, lse_part);
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  const hipError_t e =
+      mask == ATTN_MASK_NONE
+          ? launch_kernel(attn_fwd_kernel<kPartial, false, false, false, false>, grid, block, s, qq, kk, vv, oo,
+                          (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, (int64_t)0, lse_part)
+          : launch_kernel(attn_fwd_kernel<kPartial, false, true, false, false>, grid, block, s, qq, kk, vv, oo,
+                          (int)H, (int)Sq, (int)Sk, (int)pb.n_qtiles, g, sp, none, 0, off, lse_part);
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" int attn_fwd_bf16_merge(const float* o_parts, const float* lse_parts, int64_t n_parts, void* o,
@@ -1384,21 +1404,22 @@ extern "C" int attn_fwd_bf16_merge(const float* o_parts, const float* lse_parts,
   hipStream_t s = (hipStream_t)stream;
   uint16_t* oo = (uint16_t*)o;
   const int64_t part_elems = rows * D;
+  hipError_t e;
   switch (round_mode) {
     case ATTN_ROUND_RTNE:
-      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTNE>, grid, block, 0, s, o_parts, lse_parts,
-                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      e = launch_kernel(attn_merge_shards_kernel<ATTN_ROUND_RTNE>, grid, block, s, o_parts, lse_parts, (int)n_parts,
+                        part_elems, rows, (int)H, (int)Sq, g, oo, lse);
       break;
     case ATTN_ROUND_RTNA:
-      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTNA>, grid, block, 0, s, o_parts, lse_parts,
-                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      e = launch_kernel(attn_merge_shards_kernel<ATTN_ROUND_RTNA>, grid, block, s, o_parts, lse_parts, (int)n_parts,
+                        part_elems, rows, (int)H, (int)Sq, g, oo, lse);
       break;
     default:
-      hipLaunchKernelGGL(attn_merge_shards_kernel<ATTN_ROUND_RTZ>, grid, block, 0, s, o_parts, lse_parts,
-                         (int)n_parts, part_elems, rows, (int)H, (int)Sq, g, oo, lse);
+      e = launch_kernel(attn_merge_shards_kernel<ATTN_ROUND_RTZ>, grid, block, s, o_parts, lse_parts, (int)n_parts,
+                        part_elems, rows, (int)H, (int)Sq, g, oo, lse);
       break;
   }
-  return hipGetLastError() == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
+  return e == hipSuccess ? ATTN_OK : ATTN_ERR_HIP;
 }
 
 extern "C" int attn_fwd_bf16_split_plan(int64_t n_work, int64_t n_tiles, int64_t n_cu, int64_t* out4) {

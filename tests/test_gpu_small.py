@@ -196,3 +196,30 @@ def test_python_wrapper_matches_c_abi():
     assert np.array_equal(to_bits(out), ref)
     with pytest.raises(ValueError):
         attn.attn_fwd(dev.q.float(), dev.k, dev.v)
+
+
+def test_an_earlier_failed_hip_call_is_not_reported_as_a_launch_failure():
+    # A HIP call of the caller that failed earlier (here hipSetDevice with a device index that does
+    # not exist, rejected by the runtime on the host) can leave its error pending in the thread. The
+    # library reports each launch's own status, so the next call succeeds all the same.
+    import ctypes
+    import bf16_forward_attention_amd as attn
+
+    hip = ctypes.CDLL("libamdhip64.so")
+    hip.hipSetDevice.argtypes = [ctypes.c_int]
+    inp = synth.small(1, 2, 100, 130, "bshd", seed=8)
+    ex, rd = oracle.attn_all(inp.q, inp.k, inp.v, "bshd")
+    dev = Dev(inp)
+    torch.cuda.synchronize()
+    hip.hipGetLastError()  # start from a clean slate
+    assert hip.hipSetDevice(1 << 20) != 0
+    pending = hip.hipPeekAtLastError()
+    say(f"  pending error after the failed call: {pending}")
+    s = torch.cuda.current_stream()
+    st = attn.attn_fwd_bf16(dev.q.data_ptr(), dev.k.data_ptr(), dev.v.data_ptr(), dev.o.data_ptr(), 1, 2, 100, 130,
+                            attn.LAYOUTS["bshd"], attn.ROUND_MODES["rtne"], s.cuda_stream)
+    hip.hipGetLastError()  # leave the thread clean for the tests that follow
+    torch.cuda.synchronize()
+    assert st == 0, attn.attn_fwd_bf16_strerror(st)
+    got = np.ascontiguousarray(synth.to_logical(to_bits(dev.o), "bshd"))
+    assert gate(got, rd[0], ex).ok
