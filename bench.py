@@ -20,7 +20,8 @@ BSHD, RTNE.  Prints one JSON line:
   clock      the shader clock of each XCD and the socket power (amd-smi) during
              about 4 s more of the same launches right after the timed region, and
              the rate over the last 2 s of them (sustained_tflops)
-  env        ROCm and torch versions, the device, the hipcc flags of the build
+  env        ROCm and torch versions, the device, the hipcc flags of the build and the
+             hash of the kernel source (the one the profiles/ summaries name)
   sweep      (with the default workload, or --sweep; under rocprofv3 only with --sweep)
              the other configurations of 8K and longer, each timed alone the same way
              after the headline: the 128K long-context workload in all three rounding
@@ -188,7 +189,7 @@ def run_env(dev) -> dict:
         rocm = None
     return {"rocm": rocm, "torch": torch.__version__, "hip": torch.version.hip, "device": p.name,
             "arch": p.gcnArchName, "cus": p.multi_processor_count,
-            "hipcc_flags": " ".join(build.HIPCC_FLAGS)}
+            "hipcc_flags": " ".join(build.HIPCC_FLAGS), "kernel_code_sha256": kernel_code_sha256()}
 
 
 def parse():
