@@ -15,6 +15,7 @@ only, every step of the computation runs in the HIP library
     attn_fwd_bf16_gqa_ws(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, ws, ws_bytes,
                          stream) -> status
     attn_fwd_bf16_gqa_workspace_size(B, H, Sq, Sk, mask) -> bytes
+    attn_fwd_bf16_gqa_noalloc(q, k, v, o, lse, B, H, H_kv, Sq, Sk, layout, round_mode, mask, stream) -> status
     attn_fwd_bf16_partial(q, k, v, o_part, lse_part, B, H, H_kv, Sq, Sk, key_offset, Sk_total, layout, mask,
                           stream) -> status
     attn_fwd_bf16_merge(o_parts, lse_parts, n_parts, o, lse, B, H, Sq, layout, round_mode, stream) -> status
