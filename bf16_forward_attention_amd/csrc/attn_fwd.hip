@@ -137,6 +137,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8_t;
 constexpr int kHookAt0 = 1, kHookAt1 = 9;
 // log2(e) / sqrt(128), rounded to fp32
 constexpr float kScaleLog2 = 0.12751743082459868f;
+// 1 / kScaleLog2, rounded to fp32: turns a threshold on scaled logits into one on raw logits
+constexpr float kInvScaleLog2 = 7.84206485748291f;
 // gfx9 buffer descriptor word 3: 32-bit data format, no swizzle, raw addressing
 constexpr int kBufferWord3 = 0x00020000;
 
@@ -495,6 +497,10 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
   for (int db = 0; db < 4; ++db) acc[db] = f32x16{};
   float m_run = -3.402823466e38f;
   float l_run = 0.0f;
+  // the raw logit past which the running maximum moves: (m_run + 8) / c in
+  // fp32, kept with m_run (-Inf while m_run is -FLT_MAX: any finite logit
+  // moves it then)
+  float m_thr = -__builtin_inff();
 
   f32x16 S[2][2];      // logits of two tiles: the one being turned into weights, the next one
   bf16x8 pf[2][2];     // weights of the current tile, the B operand of P.V
@@ -539,23 +545,25 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
       for (int n = 0; n < 16; ++n) m = fmaxf(m, s[kb][n]);
     mx = m;
   };
-  // Move the running maximum when some row's maximum grew past 2^8.  Whether
-  // any row did is decided from each lane's half of its row (a row's maximum
-  // grew past the threshold iff one of its halves did), so the exchange
-  // between the two halves is only needed on the rare move itself.  The
-  // candidate is the scaled row maximum rounded up by at least half an ulp:
-  // then fma(s, c, -m) <= 0 for the maximal logit, its weight exp2(<= 0) <= 1
-  // rounds to exactly 1 in bf16, so a row dominated by one key (or with a
-  // single key) returns that V row exactly in every mode.  (-Inf / NaN maxima
-  // give NaN here, which fmaxf ignores.)
+  // Move the running maximum when some row's maximum grew past 2^8 above it:
+  // one compare of the raw maximum against m_thr per tile (m_thr carries the
+  // fp32 rounding of (m + 8) / c, so a maximum within a few ulp of the
+  // threshold may stay, and its weight reach 2^8 times 1 + a few ulp).
+  // Whether any row grew is decided from each lane's half of its row (a
+  // row's maximum grew past the threshold iff one of its halves did), so the
+  // exchange between the two halves is only needed on the rare move itself.
+  // The candidate is the scaled row maximum rounded up by at least half an
+  // ulp: then fma(s, c, -m) <= 0 for the maximal logit, its weight
+  // exp2(<= 0) <= 1 rounds to exactly 1 in bf16, so a row dominated by one
+  // key (or with a single key) returns that V row exactly in every mode.
+  // (-Inf and NaN maxima compare false; in a move, fmaxf ignores a NaN half.)
   auto rescale = [&]() __attribute__((always_inline)) {
-    const float ms = mx * kScaleLog2;
-    const float m_half = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(ms), 0x1p-23f, ms));
-    if (__builtin_amdgcn_ballot_w64(m_half > m_run + kRescaleLog2) != 0) {
+    if (__builtin_amdgcn_ballot_w64(mx > m_thr) != 0) {
       const float mr = wave_half_max(mx) * kScaleLog2;
       const float m_new = fmaxf(m_run, __builtin_fmaf(__builtin_fabsf(mr), 0x1p-23f, mr));
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
       m_run = m_new;
+      m_thr = (m_run + kRescaleLog2) * kInvScaleLog2;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db) acc[db] *= alpha;
@@ -583,7 +591,8 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
       f32x2 p;
       p[0] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][n], kScaleLog2, -m_run));
       p[1] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[kb][n + 1], kScaleLog2, -m_run));
-      psum += p[0];
+      // (weights are >= +0, so starting from the first one equals 0 + it)
+      psum = i == 0 ? p[0] : psum + p[0];
       psum += p[1];
       const bf16x2 pb = __builtin_convertvector(p, bf16x2);
       pf[kb][hh][2 * q2] = pb[0];
