@@ -537,8 +537,13 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
       for (int n = 0; n < 16; ++n)
         if (32 * kb + n > rel) s[kb][n] = -__builtin_inff();
   };
+  // (the reductions start from -Inf, which fmaxf drops, so that they are all
+  // v_max3: starting from the first logit made this compiler quiet the first
+  // two logits with v_max x,x and pair them with a third v_max.  A half row
+  // of NaN or -Inf logits now gives -Inf where it gave NaN; both compare
+  // false in the rescale test and drop out of a move.)
   auto rowmax = [&](const f32x16 (&s)[2]) __attribute__((always_inline)) {
-    float m = s[0][0];
+    float m = -__builtin_inff();
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -618,7 +623,7 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
     };
 #pragma unroll
     for (int i = 0; i < 4; ++i) vread(i);
-    float m = sn[0][0];
+    float m = -__builtin_inff();
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       if (i + 4 < 16) vread(i + 4);
