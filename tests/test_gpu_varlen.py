@@ -84,6 +84,58 @@ def test_each_sequence_matches_the_fixed_length_entry_point(mask):
         assert np.array_equal(to_bits(o)[0], got[q0:q1]), b
 
 
+# Larger causal batches: grids of at least two rounds of 256 compute units (H=32 query heads over
+# 8 K/V heads), sequences of odd and even q-tile counts (513, 1 and 256 rows have 3, 1 and 1),
+# sequences without queries and without keys, bottom-right diagonals with Sk > Sq and Sk < Sq.
+LARGE = [
+    # (lengths_q, lengths_k, mask)
+    ((1, 300, 0, 777, 1500, 513, 256), (1, 300, 0, 777, 1500, 513, 256), "causal"),
+    ((1, 300, 0, 777, 1500, 513, 256), (5, 700, 10, 600, 1500, 2000, 0), "causal_br"),
+]
+
+
+def _grid(wl, max_q):
+    n_qt = -(-max_q // 256)
+    return 8 * -(-wl.B * wl.H_kv // 8) * (wl.H // wl.H_kv) * n_qt
+
+
+@pytest.mark.parametrize("case", range(len(LARGE)))
+def test_large_causal_varlen_all_rows(case):
+    lq, lk, mask = LARGE[case]
+    wl = synth.VarlenWorkload(f"varlen_large{case}", lq, lk, 32, 8, MODES, mask=mask, seed=41 + case)
+    assert _grid(wl, max(lq)) >= 2 * 256, "the case must fill two rounds of compute units"
+    inp = synth.generate_varlen(wl)
+    ex, rd = oracle.attn_all_varlen(inp.q, inp.k, inp.v, inp.cu_q, inp.cu_k, mask)
+    for m, mode in enumerate(MODES):
+        got = _run(inp, mode, mask)
+        res = gate(got, rd[m], ex)
+        say(f"  varlen_large{case} {mask} {mode}: {res.summary()}")
+        assert res.ok, f"varlen_large{case} {mask} {mode}: {res.summary()}"
+    # a larger max_seqlen_q only adds workgroups past every sequence's end
+    assert np.array_equal(_run(inp, MODES[0], mask, max_q=3 * max(lq) + 7), _run(inp, MODES[0], mask))
+
+
+@pytest.mark.parametrize("mask", ["causal", "causal_br"])
+def test_large_causal_varlen_sequences_match_the_fixed_length_entry_point(mask):
+    # each sequence alone through attn_fwd_bf16_gqa: the same arithmetic on the same rows, so the
+    # same bits
+    lq = (513, 64, 1025, 300)
+    lk = lq if mask == "causal" else (700, 64, 1100, 1000)
+    wl = synth.VarlenWorkload(f"varlen_large_eq_{mask}", lq, lk, 32, 8, MODES, mask=mask, seed=51)
+    assert _grid(wl, max(lq)) >= 2 * 256
+    inp = synth.generate_varlen(wl)
+    got = _run(inp, "rtne", mask)
+    for b in range(wl.B):
+        q0, q1, k0, k1 = inp.cu_q[b], inp.cu_q[b + 1], inp.cu_k[b], inp.cu_k[b + 1]
+        q = to_device(np.ascontiguousarray(inp.q[q0:q1][None]))
+        k = to_device(np.ascontiguousarray(inp.k[k0:k1][None]))
+        v = to_device(np.ascontiguousarray(inp.v[k0:k1][None]))
+        o = torch.empty_like(q)
+        launch_gqa(q, k, v, o, "bshd", "rtne", mask)
+        torch.cuda.synchronize()
+        assert np.array_equal(to_bits(o)[0], got[q0:q1]), b
+
+
 def test_offsets_outside_the_tensors_are_clamped():
     # cu_seqlens past total_q / total_k (and a decreasing pair) are clamped on the
     # device: rows outside the tensors are never touched and sequence 0 stays right
