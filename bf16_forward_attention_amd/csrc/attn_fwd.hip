@@ -829,10 +829,10 @@ __device__ __forceinline__ void attn_item(const uint16_t* __restrict__ Q, const 
   } else {
     // Without a mask every iteration runs whole: the last one also computes
     // the logits of a tile that does not exist, and never uses them (peeling
-    // that iteration here measured 0.7-1.0% slower, on long items too: it
-    // changes how this compiler schedules the loop).  Written as an exit test
-    // after each body: a test before the first one makes this compiler spill
-    // the pipeline's registers.
+    // that iteration here, in two forms, measured 0.5-1.0% slower, on long
+    // items too: it changes how this compiler lays out the loop).  Written as
+    // an exit test after each body: a test before the first one makes this
+    // compiler spill the pipeline's registers.
     for (int t = 0;;) {
       body(S0{}, Plain{}, t);
       if (++t == n_tiles) break;
