@@ -237,6 +237,17 @@ def _dims(q, k, layout: str):
     return B, H, Hk, Sq, Sk
 
 
+def _record_on(s, stream, *tensors):
+    """Tensors allocated here on torch's current stream but written on a caller's other stream:
+    tell torch's caching allocator, so that their memory is not handed out again before that
+    stream is done with it."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(s)
+
+
 def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", stream=None,
              split: bool = True, mask: str = "none", with_lse: bool = False):
     """O = softmax(Q K^T / sqrt(128)) V on bf16 CUDA(HIP) tensors.
@@ -266,7 +277,8 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
             raise ValueError(f"{name} must be a contiguous bfloat16 GPU tensor")
         if t.device != q.device:
             raise ValueError("q, k and v must be on one device")
-    if out is None:
+    own_out = out is None
+    if own_out:
         out = torch.empty_like(q)
     elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous()
           or out.device != q.device):
@@ -302,6 +314,7 @@ def attn_fwd(q, k, v, out=None, layout: str = "bshd", round_mode: str = "rtne", 
         else:
             status = attn_fwd_bf16(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, H, Sq, Sk,
                                    LAYOUTS[layout], ROUND_MODES[round_mode], s.cuda_stream)
+        _record_on(s, stream, out if own_out else None, lse)
     if status != 0:
         raise AttnError(status)
     return (out, lse) if with_lse else out
@@ -331,10 +344,12 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, out=
         raise ValueError("cu_seqlens_q and cu_seqlens_k must both hold B+1 >= 2 offsets")
     total_q, H, _ = q.shape
     total_k, H_kv, _ = k.shape
-    if out is None:
+    own_out = out is None
+    if own_out:
         out = torch.empty_like(q)
-    elif out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous():
-        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q")
+    elif (out.dtype != torch.bfloat16 or tuple(out.shape) != tuple(q.shape) or not out.is_contiguous()
+          or out.device != q.device):
+        raise ValueError("out must be a contiguous bfloat16 tensor shaped like q on q's device")
     lse = torch.empty((H, total_q), dtype=torch.float32, device=q.device) if with_lse else None
     with torch.cuda.device(q.device):
         s = stream if stream is not None else torch.cuda.current_stream(q.device)
@@ -343,6 +358,7 @@ def attn_fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, out=
                                       cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), cu_seqlens_q.numel() - 1,
                                       H, H_kv, total_q, total_k, max_seqlen_q, ROUND_MODES[round_mode], MASKS[mask],
                                       s.cuda_stream)
+        _record_on(s, stream, out if own_out else None, lse)
     if status != 0:
         raise AttnError(status)
     return (out, lse) if with_lse else out

@@ -198,6 +198,30 @@ def test_python_wrapper_matches_c_abi():
         attn.attn_fwd(dev.q.float(), dev.k, dev.v)
 
 
+def test_python_wrappers_on_a_caller_stream():
+    # the torch-level calls enqueue on a stream the caller passes (not torch's current one) and
+    # give the bits of the C ABI, with and without the log-sum-exp, fixed-length and packed
+    import bf16_forward_attention_amd as attn
+    inp = synth.small(2, 4, 300, 300, "bshd", seed=9)
+    dev = Dev(inp)
+    ref = dev.run("rtne")
+    s = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    out = attn.attn_fwd(dev.q, dev.k, dev.v, layout="bshd", round_mode="rtne", stream=s, split=False)
+    out2, lse = attn.attn_fwd(dev.q, dev.k, dev.v, layout="bshd", round_mode="rtne", stream=s, split=False,
+                              with_lse=True)
+    s.synchronize()
+    assert np.array_equal(to_bits(out), ref)
+    assert np.array_equal(to_bits(out2), ref)
+    assert lse.shape == (2, 4, 300) and bool(torch.isfinite(lse).all())
+    # the same rows packed as two sequences of 300
+    qp, kp, vp = (t.reshape(600, 4, 128) for t in (dev.q, dev.k, dev.v))
+    cu = torch.tensor([0, 300, 600], dtype=torch.int32, device=qp.device)
+    outp = attn.attn_fwd_varlen(qp, kp, vp, cu, cu, 300, round_mode="rtne", stream=s)
+    s.synchronize()
+    assert np.array_equal(to_bits(outp).reshape(2, 300, 4, 128), ref)
+
+
 def test_an_earlier_failed_hip_call_is_not_reported_as_a_launch_failure():
     # A HIP call of the caller that failed earlier (here hipSetDevice with a device index that does
     # not exist, rejected by the runtime on the host) can leave its error pending in the thread. The
