@@ -1052,9 +1052,17 @@ constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch_state[kMaxDevices];  // 0 unknown, 1 gfx950, 2 other
 std::atomic<int> g_cu_count[kMaxDevices];    // 0 unknown
 
-int check_device(int* n_cu) {
+// The current device must be gfx950 (its CU count is cached), and a stream the
+// caller passes must belong to it: the split plans use this device's CU count
+// and the static scratch is this device's.  A stream whose device cannot be
+// queried is taken as it is.
+int check_device(int* n_cu, void* stream = nullptr) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return ATTN_ERR_DEVICE;
+  if (stream) {
+    hipDevice_t sdev = -1;
+    if (hipStreamGetDevice((hipStream_t)stream, &sdev) == hipSuccess && sdev != dev) return ATTN_ERR_DEVICE;
+  }
   if (dev < kMaxDevices) {
     const int st = g_arch_state[dev].load(std::memory_order_acquire);
     if (st == 2) return ATTN_ERR_DEVICE;
@@ -1327,7 +1335,7 @@ extern "C" int attn_fwd_bf16(const void* q, const void* k, const void* v, void* 
   const int st = check_args(q, k, v, o, B, H, H, Sq, Sk, layout, round_mode, &pb);
   if (st != ATTN_OK) return st;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
   return run(q, k, v, o, H, H, Sq, Sk, layout, round_mode, ATTN_MASK_NONE, pb, whole, nullptr, stream, n_cu);
@@ -1350,7 +1358,7 @@ extern "C" int attn_fwd_bf16_gqa(const void* q, const void* k, const void* v, vo
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_MASK;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan whole{pb.n_work, 0, 1, pb.n_tiles};
   return run(q, k, v, o, H, H_kv, Sq, Sk, layout, round_mode, mask, pb, whole, nullptr, stream, n_cu, nullptr, lse);
@@ -1405,7 +1413,7 @@ extern "C" int attn_fwd_bf16_varlen(const void* q, const void* k, const void* v,
   int64_t n_wg;
   if (!mul_ok(8 * ((n_groups + 7) / 8), per_group, &n_wg) || n_wg > INT32_MAX - 65536) return ATTN_ERR_SIZE;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   const Varlen vl{cu_seqlens_q, cu_seqlens_k, (int)total_q, (int)total_k, (int)n_groups};
   pb.n_work = n_wg;
@@ -1433,7 +1441,7 @@ extern "C" int attn_fwd_bf16_partial(const void* q, const void* k, const void* v
   if (mask != ATTN_MASK_NONE && mask != ATTN_MASK_CAUSAL && mask != ATTN_MASK_CAUSAL_BOTTOM_RIGHT)
     return ATTN_ERR_MASK;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   // row i sees the global keys j <= i + off_global; this shard's key j is
   // global key key_offset + j
@@ -1476,7 +1484,7 @@ extern "C" int attn_fwd_bf16_merge(const float* o_parts, const float* lse_parts,
                overlaps(lse, rows * 4, o, o_bytes))))
     return ATTN_ERR_ALIAS;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   const Geometry g = make_geometry(H, H, Sq, 1, layout);
   const int64_t threads = rows * (D / 4);
@@ -1584,7 +1592,7 @@ int gqa_split_call(const void* q, const void* k, const void* v, void* o, float* 
     return ATTN_ERR_MASK;
   if (workspace_bytes < 0) return ATTN_ERR_SIZE;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   const Plan plan = make_plan_masked(pb.n_work, pb.n_qtiles, Sq, Sk, mask, n_cu);
   const int64_t need = plan_workspace_bytes(plan);
@@ -1627,7 +1635,7 @@ extern "C" int attn_fwd_bf16_ws(const void* q, const void* k, const void* v, voi
   if (st != ATTN_OK) return st;
   if (workspace_bytes < 0) return ATTN_ERR_SIZE;
   int n_cu = 0;
-  const int dev_status = check_device(&n_cu);
+  const int dev_status = check_device(&n_cu, stream);
   if (dev_status != ATTN_OK) return dev_status;
   Plan plan = make_plan(pb.n_work, pb.n_tiles, n_cu);
   const int64_t need = plan_workspace_bytes(plan);
@@ -1651,7 +1659,9 @@ extern "C" const char* attn_fwd_bf16_strerror(int status) {
     case ATTN_ERR_ROUND: return "round_mode must be ATTN_ROUND_RTNE, ATTN_ROUND_RTNA or ATTN_ROUND_RTZ";
     case ATTN_ERR_ALIGN: return "q, k, v, o and the workspace must be 16-byte aligned";
     case ATTN_ERR_ALIAS: return "o or the workspace overlaps another buffer";
-    case ATTN_ERR_DEVICE: return "the current HIP device is not gfx950 (MI355X) or cannot be queried";
+    case ATTN_ERR_DEVICE:
+      return "the current HIP device is not gfx950 (MI355X) or cannot be queried, or the stream belongs to another "
+             "device";
     case ATTN_ERR_HIP: return "the HIP kernel launch failed";
     case ATTN_ERR_WORKSPACE: return "the workspace is smaller than attn_fwd_bf16_workspace_size reports";
     case ATTN_ERR_MASK: return "mask is not an attn_mask_t value";

@@ -75,7 +75,7 @@ typedef enum {
     ATTN_ERR_ROUND = 4,  /* round_mode is not an attn_round_t value */
     ATTN_ERR_ALIGN = 5,  /* a pointer is not 16-byte aligned */
     ATTN_ERR_ALIAS = 6,  /* o overlaps q, k or v */
-    ATTN_ERR_DEVICE = 7, /* the current device is not gfx950, or cannot be queried */
+    ATTN_ERR_DEVICE = 7, /* the current device is not gfx950 or cannot be queried, or the stream is another device's */
     ATTN_ERR_HIP = 8,    /* the kernel launch failed */
     ATTN_ERR_WORKSPACE = 9, /* the workspace is smaller than attn_fwd_bf16_workspace_size reports */
     ATTN_ERR_MASK = 10,     /* mask is not an attn_mask_t value */
@@ -92,16 +92,18 @@ typedef enum {
  *   Sq, Sk  : query and key lengths (>= 1), independent of each other.
  *   layout  : attn_layout_t, shared by all four tensors.
  *   round_mode : attn_round_t, the output rounding.
- *   stream  : hipStream_t to enqueue on (NULL = the null stream).
+ *   stream  : hipStream_t of the current device to enqueue on (NULL = its
+ *             null stream).
  *
  * Returns ATTN_OK once the kernel is enqueued; the call is asynchronous and
  * O is valid after the stream reaches that point.  Argument errors
  * (ATTN_ERR_NULL .. ATTN_ERR_ALIAS) are detected before any HIP call and
- * nothing is launched.  ATTN_ERR_DEVICE: the current device is not gfx950.
- * ATTN_ERR_HIP: the launch was rejected (read with hipGetLastError right after
- * the launches, so an earlier error of the calling thread that nobody read is
- * reported here too, and cleared).  Faults inside the kernel surface at the
- * caller's next synchronisation, as for any HIP kernel.
+ * nothing is launched.  ATTN_ERR_DEVICE: the current device is not gfx950, or
+ * the stream belongs to another device (checked with hipStreamGetDevice).
+ * ATTN_ERR_HIP: a launch was rejected (each launch's own status; an earlier
+ * error of the calling thread is neither reported nor cleared).  Faults inside
+ * the kernel surface at the caller's next synchronisation, as for any HIP
+ * kernel.
  */
 int attn_fwd_bf16(const void *q, const void *k, const void *v, void *o,
                   int64_t B, int64_t H, int64_t Sq, int64_t Sk,
