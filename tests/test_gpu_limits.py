@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from tests.gate import gate
-from tests.gpu_util import MODES, launch, launch_gqa, say, to_bits
+from tests.gpu_util import launch, launch_gqa, say
 
 pytestmark = pytest.mark.gpu
 
